@@ -1,0 +1,237 @@
+"""Pins for the oracle's quantize / dequantize / GEMM reference (CPU only).
+
+The checks are invariants the pages fix or the mathematics forces:
+  * exact round trip of values that are already representable;
+  * the tensor-scale reading: the block holding the tensor's amax encodes to 448;
+  * 16x16 blocks quantize W and W^T identically (prism article, section on training
+    stability and sensitive layers);
+  * scale-array shapes follow the 16-element micro-block (NVIDIA blog, recipe bullet 1);
+  * the round-to-nearest error bound and unbiased stochastic rounding;
+  * the GEMM reference equals an exact rational brute force on a tiny product.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from block_scaled_fp4_06_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FACTS = json.load(open(os.path.join(HERE, "golden", "pages_facts.json")))
+MAGS = np.array(FACTS["e2m1_magnitudes"]["value"])
+
+
+def e2m1_val(q):
+    q = np.asarray(q)
+    return np.where(q & 8, -1.0, 1.0) * MAGS[q & 7]
+
+
+def unpack(codes):
+    lo = codes & 0x0F
+    hi = codes >> 4
+    out = np.empty((codes.shape[0], codes.shape[1] * 2), np.uint8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def e4m3_table(orc):
+    return orc.e4m3_decode(np.arange(127, dtype=np.uint8)).astype(np.float64)
+
+
+def representable_tensor(orc, rows, cols, blocking, seed, s_dec_log2=-3):
+    """A bf16 tensor whose every value is e2m1 * sbd * s_dec with s_dec = 2^k, every
+    block holding one element of magnitude 6 * sbd and one block with sbd = 448."""
+    rng = np.random.default_rng(seed)
+    tab = e4m3_table(orc)
+    bh = 16 if blocking == orc.BLOCK_16x16 else 1
+    nbr, nbc = rows // bh, cols // 16
+    sidx = rng.integers(40, 127, (nbr, nbc))
+    sidx[0, 0] = 126
+    sbd = tab[sidx]
+    q = rng.integers(0, 16, (rows, cols))
+    for br in range(nbr):
+        for bc in range(nbc):
+            r = br * bh + rng.integers(0, bh)
+            c = bc * 16 + rng.integers(0, 16)
+            q[r, c] = 7 | (8 * rng.integers(0, 2))
+    s_dec = 2.0 ** s_dec_log2
+    full_sbd = np.repeat(np.repeat(sbd, bh, axis=0), 16, axis=1)
+    x = e2m1_val(q) * full_sbd * s_dec
+    xb = W.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(xb).astype(np.float64), x)  # exactly bf16
+    return xb, q, sidx.astype(np.uint8), s_dec
+
+
+@pytest.mark.parametrize("blocking", [0, 1])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_round_trip_of_representable_values(orc, blocking, rounding):
+    rows, cols = 64, 128
+    xb, q, sidx, s_dec = representable_tensor(orc, rows, cols, blocking, seed=blocking * 2 + rounding)
+    codes, scales, g, st = orc.quantize(xb, blocking=blocking, rounding=rounding, sr_seed=9)
+    assert st == 0
+    assert g == np.float32(s_dec)
+    assert np.array_equal(scales, sidx)
+    got = unpack(codes)
+    assert np.array_equal(e2m1_val(got), e2m1_val(q))  # +-0 may differ only in sign
+    y = orc.dequantize(codes, scales, g, rows, cols, blocking)
+    assert np.array_equal(y, W.bf16_bits_to_f32(xb))
+
+
+def test_scale_shapes_follow_micro_blocks(orc):
+    n = FACTS["micro_block_elements"]["value"]
+    x = W.w1()
+    codes, scales, g, st = orc.quantize(x)
+    assert codes.shape == (256, 256 // 2) and scales.shape == (256, 256 // n)
+    wb = FACTS["weight_block"]
+    codes, scales, g, st = orc.quantize(x, blocking=orc.BLOCK_16x16)
+    assert scales.shape == (256 // wb["rows"], 256 // wb["cols"])
+    assert wb["rows"] * wb["cols"] == wb["values_per_scale"]
+
+
+@pytest.mark.parametrize("blocking,rht", [(0, False), (0, True), (1, False)])
+def test_global_scale_reading(orc, blocking, rht):
+    """s_dec = amax / (6 * 448): the block holding the tensor amax gets scale 448."""
+    x = W.w1()
+    codes, scales, g, st = orc.quantize(x, blocking=blocking, rht=rht, rht_seed=W.RHT_SEED)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    if rht:
+        xf = orc.rht16(xf.astype(np.float32).ravel(), W.RHT_SEED).reshape(xf.shape).astype(np.float64)
+    amax = np.abs(xf).max()
+    assert abs(float(g) * 2688.0 - amax) <= amax * 2.0 ** -23
+    r, c = np.unravel_index(np.abs(xf).argmax(), xf.shape)
+    bh = 16 if blocking else 1
+    assert scales[r // bh, c // 16] == 0x7E
+    assert scales.max() == 0x7E
+
+
+def test_w_and_wt_quantize_identically_16x16(orc):
+    """PR, training stability section: 2D 16x16 blocks make W and W^T agree."""
+    w = W.normal_scaled(512, 768, seed=2, std=0.02)
+    c1, s1, g1, _ = orc.quantize(w, blocking=orc.BLOCK_16x16)
+    c2, s2, g2, _ = orc.quantize(np.ascontiguousarray(w.T), blocking=orc.BLOCK_16x16)
+    assert g1 == g2
+    assert np.array_equal(s2, s1.T)
+    assert np.array_equal(unpack(c2), unpack(c1).T)
+    # 1x16 blocks do not have this property
+    c3, s3, _, _ = orc.quantize(w)
+    c4, s4, _, _ = orc.quantize(np.ascontiguousarray(w.T))
+    assert not np.array_equal(unpack(c4), unpack(c3).T)
+
+
+def test_rn_error_bound(orc):
+    """Every element not clipped at 6: |v - q| <= half the local grid step, where
+    v = y * s_enc / sbd is the value in code units."""
+    x = W.w1()
+    codes, scales, g, _ = orc.quantize(x)
+    y = W.bf16_bits_to_f32(x).astype(np.float64)
+    tab = e4m3_table(orc)
+    sbd = np.repeat(tab[scales], 16, axis=1)
+    s_enc = np.float32(2688.0) / np.float32(np.abs(y).max())
+    r = (np.float32(s_enc) / sbd.astype(np.float32)).astype(np.float32)
+    v = (y.astype(np.float32) * r).astype(np.float64)
+    q = e2m1_val(unpack(codes))
+    a = np.abs(v)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    ok = (a <= 6) & (np.abs(v - q) <= step / 2)
+    clipped = a > 6
+    assert np.all(ok | clipped)
+    assert np.all(q[clipped] == np.sign(v[clipped]) * 6)
+    # per-block max error of the dequantized tensor (fp32 dequant), C1-style report
+    xh = orc.dequantize(codes, scales, g, 256, 256)
+    err = np.abs(xh - y).reshape(256, 16, 16).max(axis=2)
+    bound = (sbd[:, ::16] * float(g)) * 1.0 + 1e-30  # half of the largest step (2) * sbd * s_dec
+    assert np.all(err <= bound * (1 + 2.0 ** -20))
+
+
+def test_zero_and_nonfinite_inputs(orc):
+    z = np.zeros((32, 32), np.uint16)
+    codes, scales, g, st = orc.quantize(z)
+    assert st == 0 and g == 1.0 and not scales.any() and not codes.any()
+    negz = np.full((32, 32), 0x8000, np.uint16)  # -0.0
+    codes, scales, g, st = orc.quantize(negz)
+    assert np.all(codes == 0x88)  # the sign bit is kept
+    x = W.w1().copy()
+    x[3, 5] = 0x7F80  # +inf
+    codes, scales, g, st = orc.quantize(x)
+    assert st == 1 and np.isnan(g)
+    x[3, 5] = 0x7FC0  # NaN
+    _, _, g, st = orc.quantize(x, rht=True, rht_seed=1)
+    assert st == 1 and np.isnan(g)
+
+
+def test_bad_arguments(orc):
+    with pytest.raises(orc.QuantizeError):
+        orc.quantize(np.zeros((16, 24), np.uint16))
+    with pytest.raises(orc.QuantizeError):
+        orc.quantize(np.zeros((16, 16), np.uint16), blocking=1, rht=True)
+    with pytest.raises(orc.QuantizeError):
+        orc.quantize(np.zeros((16, 16), np.uint16), rounding=1, sr_index_base=8)
+
+
+def test_sr_chunking_equals_whole(orc):
+    """Philox is keyed on (seed, element index): two half-tensors quantized with
+    sr_index_base equal one call over the whole (same tensor amax in both halves)."""
+    x = W.w4(64, 256).copy()
+    x[0, 0] = 0x4000
+    x[32, 0] = 0x4000  # both halves hold the tensor amax (2.0)
+    kw = dict(rounding=orc.ROUND_SR, rht=False, sr_seed=77)
+    cw, sw, gw, _ = orc.quantize(x, **kw)
+    ca, sa, ga, _ = orc.quantize(x[:32], **kw)
+    cb, sb, gb, _ = orc.quantize(x[32:], sr_index_base=32 * 256, **kw)
+    assert ga == gw == gb
+    assert np.array_equal(np.concatenate([ca, cb]), cw)
+    assert np.array_equal(np.concatenate([sa, sb]), sw)
+
+
+def test_sr_unbiased_over_seeds(orc):
+    """Workload-4 recipe at 256 x 512: the mean over 64 seeds of the stochastically
+    rounded codes matches the unrounded value in code units (z-test, 5/sqrt(n))."""
+    x = W.student_t(256, 512, seed=4)
+    nseed = 64
+    acc = None
+    for s in range(nseed):
+        codes, scales, g, _ = orc.quantize(x, rounding=orc.ROUND_SR, rht=True,
+                                           rht_seed=W.RHT_SEED, sr_seed=s)
+        q = e2m1_val(unpack(codes))
+        acc = q if acc is None else acc + q
+        if s == 0:
+            sc0, g0 = scales, g
+        assert np.array_equal(scales, sc0) and g == g0  # scales do not depend on the seed
+    mean = acc / nseed
+    y = orc.rht16(W.bf16_bits_to_f32(x).ravel(), W.RHT_SEED).reshape(x.shape)
+    tab = e4m3_table(orc).astype(np.float32)
+    s_enc = np.float32(2688.0) / np.float32(np.abs(y).max())
+    r = (s_enc / tab[np.repeat(sc0, 16, axis=1)]).astype(np.float32)
+    v = (y * r).astype(np.float64)
+    a = np.abs(v)
+    lo_idx = np.clip(np.searchsorted(MAGS, a, side="right") - 1, 0, 6)
+    lo, hi = MAGS[lo_idx], MAGS[lo_idx + 1]
+    p = (a - lo) / (hi - lo)
+    use = (a < 6) & (p > 0) & (p < 1)
+    z = (np.abs(mean) - a)[use] / np.sqrt((hi - lo)[use] ** 2 * p[use] * (1 - p[use]) / nseed)
+    n = z.size
+    assert n > 10000
+    assert abs(z.mean()) <= 5 / np.sqrt(n), z.mean()
+
+
+def test_gemm_reference_exact_bruteforce(orc):
+    rng = np.random.default_rng(8)
+    a = W.f32_to_bf16_bits(rng.standard_normal((16, 32), dtype=np.float32))
+    b = W.f32_to_bf16_bits(rng.standard_normal((32, 32), dtype=np.float32))
+    qa = orc.quantize(a, rht=True, rht_seed=5)
+    qb = orc.quantize(b, blocking=orc.BLOCK_16x16)
+    c = orc.gemm_reference((qa[0], qa[1], qa[2], 16, 32, 0), (qb[0], qb[1], qb[2], 32, 32, 1))
+    tab = e4m3_table(orc)
+    va, vb = e2m1_val(unpack(qa[0])), e2m1_val(unpack(qb[0]))
+    for m in range(16):
+        for n in range(32):
+            s = Fraction(0)
+            for k in range(32):
+                fa = Fraction(va[m, k]) * Fraction(tab[qa[1][m, k // 16]])
+                fb = Fraction(vb[n, k]) * Fraction(tab[qb[1][n // 16, k // 16]])
+                s += fa * fb
+            exact = s * Fraction(float(qa[2])) * Fraction(float(qb[2]))
+            assert abs(Fraction(c[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
