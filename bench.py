@@ -1,0 +1,261 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step = one NVFP4 linear-layer pass over the workload-5 shapes, every kernel of the
+path once:
+  quantize X   8192 x 5120 bf16 activations, 16-point RHT + 1x16 blocks, nearest-even
+  quantize W   5120 x 20480 bf16 weight, 16x16 blocks, W and W^T codes from one read
+  GEMM         C = X_q . (W^T)_q^T, 8192 x 20480 x 5120, fp32 accumulate, bf16 out
+  dequantize   X_q -> bf16
+Inputs are seeded synthetic tensors resident in HBM before timing starts.  The printed
+JSON line carries the step throughput (GEMM FLOP per step / step time), per-kernel
+times from HIP events recorded on the launch stream, the roofline of the dominant
+kernel, standalone quantize figures for workloads 2-4 (input buffers rotated so the
+256 MB Infinity Cache cannot hold them), and the CPU oracle's rate on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-micro]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense fp4 (context only: NVFP4's E4M3-per-16 scales
+                                # cannot be applied by gfx950's E8M0-per-32 FP4 MFMA)
+METRIC = "NVFP4 quantize GB/s (% HBM peak); NVFP4 GEMM TFLOP/s (% MFMA peak)"
+M, K, NN = 8192, 5120, 20480
+
+
+def quant_bytes(rows, cols, blocking, transpose=False):
+    """Algorithmic bytes: bf16 input read once + packed codes + E4M3 scales + 4 B."""
+    n = rows * cols
+    sc = n // 256 if blocking == "16x16" else n // 16
+    out = n // 2 + sc
+    return 2 * n + out * (2 if transpose else 1) + 4
+
+
+def dequant_bytes(rows, cols, blocking, out_bytes=2):
+    n = rows * cols
+    sc = n // 256 if blocking == "16x16" else n // 16
+    return n // 2 + sc + 4 + n * out_bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-micro", action="store_true")
+    ap.add_argument("--context", action="store_true", help="also time torch fp16 matmul")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def to_dev(x_u16):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Timer:
+    """Accumulates HIP-event time of named launches on the current stream."""
+
+    def __init__(self):
+        self.ev = {}
+
+    def run(self, name, fn):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.ev.setdefault(name, []).append((a, b))
+        return r
+
+    def avg_ms(self, name):
+        pairs = self.ev[name]
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+
+def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
+    """Standalone quantize of workloads 2-4 with rotated input buffers."""
+    import torch
+    res = {}
+    cases = [
+        ("w2_16x16_wt", W.w2(), dict(blocking="16x16", with_transpose=True), "16x16", True),
+        ("w3_rht_1x16_rne", W.w3(), dict(rht=True, rht_seed=W.RHT_SEED), "1x16", False),
+        ("w4_rht_1x16_sr", W.w4(), dict(rht=True, rht_seed=W.RHT_SEED, rounding="sr", sr_seed=7),
+         "1x16", False),
+    ]
+    for name, x, kw, blk, tr in cases:
+        xd = to_dev(x)
+        nb = max(2, -(-nbuf_bytes // (xd.numel() * 2)))
+        bufs = [xd] + [xd.clone() for _ in range(nb - 1)]
+        q = N.quantize(xd, **kw)
+        for i in range(5):
+            N.quantize(bufs[i % nb], out=q, **kw)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            N.quantize(bufs[i % nb], out=q, **kw)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1000.0 / iters
+        by = quant_bytes(x.shape[0], x.shape[1], blk, tr)
+        res[name] = {"us": round(us, 2), "GBps": round(by / us / 1e3, 1),
+                     "frac": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": by,
+                     "buffers": nb}
+        log("micro %s: %.2f us, %.1f GB/s" % (name, us, by / us / 1e3))
+        del bufs, xd, q
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(x_np, w_np, sample_rows=1024):
+    """The oracle timed on this host on a bounded sample of one step (scaled to a step)."""
+    import oracle
+    from block_scaled_fp4_06_amd import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = min(threads, os.cpu_count() or 1)
+    xs = np.ascontiguousarray(x_np[:sample_rows])
+    t0 = time.perf_counter()
+    ca, sa, ga, _ = oracle.quantize(xs, rht=True, rht_seed=W.RHT_SEED)
+    t1 = time.perf_counter()
+    cw, sw, gw, _ = oracle.quantize(w_np, blocking=oracle.BLOCK_16x16)
+    wt = np.ascontiguousarray(w_np.T)
+    cwt, swt, _, _ = oracle.quantize(wt, blocking=oracle.BLOCK_16x16)
+    t2 = time.perf_counter()
+    c = oracle.gemm_reference((ca, sa, ga, sample_rows, K, 0), (cwt, swt, gw, NN, K, 1))
+    t3 = time.perf_counter()
+    oracle.dequantize_bf16(ca, sa, ga, sample_rows, K)
+    t4 = time.perf_counter()
+    del c
+    scale = M / sample_rows
+    t_step = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale + (t4 - t3) * scale
+    flops = 2.0 * M * NN * K
+    return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of %d activation rows quantized, GEMM'd (binary64) and dequantized, "
+                      "full weight quantized (W and W^T); times scaled to one step; "
+                      "%.1f s of CPU work" % (sample_rows, M, t4 - t0),
+            "seconds_per_step_est": round(t_step, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_scaled_fp4_06_amd import nvfp4 as N
+    from block_scaled_fp4_06_amd import workloads as W
+    N.load()
+    log("generating inputs")
+    x_np = W.w3()
+    w_np = W.w5_weight()
+    X = to_dev(x_np)
+    Wd = to_dev(w_np)
+    qx = N.quantize(X, rht=True, rht_seed=W.RHT_SEED)
+    qw = N.quantize(Wd, blocking="16x16", with_transpose=True)
+    C = torch.empty((M, NN), dtype=torch.bfloat16, device="cuda")
+    Xh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(t=None):
+        run = (lambda n, f: t.run(n, f)) if t is not None else (lambda n, f: f())
+        run("quantize_x", lambda: N.quantize(X, rht=True, rht_seed=W.RHT_SEED, out=qx))
+        run("quantize_w", lambda: N.quantize(Wd, blocking="16x16", with_transpose=True, out=qw))
+        run("gemm", lambda: N.gemm(qx, qw.transposed(), out=C))
+        run("dequantize_x", lambda: N.dequantize(qx, torch.bfloat16, out=Xh))
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    # per-kernel times: a second timed pass with events between the launches
+    tm = Timer()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    kern = {}
+    flops = 2.0 * M * NN * K
+    for name, by, unit in (("quantize_x", quant_bytes(M, K, "1x16"), "GB/s"),
+                           ("quantize_w", quant_bytes(K, NN, "16x16", True), "GB/s"),
+                           ("gemm", flops, "TFLOP/s"),
+                           ("dequantize_x", dequant_bytes(M, K, "1x16"), "GB/s")):
+        t = tm.avg_ms(name)
+        if unit == "GB/s":
+            ach = by / (t * 1e-3) / 1e9
+            kern[name] = {"ms": round(t, 4), "GBps": round(ach, 1),
+                          "frac_hbm": round(ach / HBM_PEAK_GBPS, 4), "bytes": by}
+        else:
+            ach = by / (t * 1e-3) / 1e12
+            kern[name] = {"ms": round(t, 4), "TFLOPs": round(ach, 1),
+                          "frac_mfma_f16": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                          "frac_mfma_fp4_context": round(ach / MFMA_FP4_PEAK_TFLOPS, 4)}
+        log("%s: %.4f ms" % (name, t))
+    g = kern["gemm"]
+    out = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 MFMA / f32 accumulate (NVFP4 operands); f32 quantize arithmetic",
+        "data": "synthetic",
+        "config": {"workload": "NVFP4 linear layer, workload 5: quantize X 8192x5120 (RHT16, "
+                               "1x16, RNE) + quantize W 5120x20480 (16x16, W and W^T) + GEMM "
+                               "8192x20480x5120 (fp32 acc, bf16 out) + dequantize X",
+                   "M": M, "N": NN, "K": K},
+        "roofline": {"bound": "mfma", "achieved": g["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": g["frac_mfma_f16"], "traffic": None,
+                     "kernel": "gemm"},
+        "kernels": kern,
+    }
+    if not args.no_micro:
+        log("standalone quantize workloads")
+        out["quantize"] = micro_quantize(N, W)
+    if args.context:
+        a16 = torch.randn((M, K), dtype=torch.float16, device="cuda")
+        b16 = torch.randn((NN, K), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            torch.matmul(a16, b16.T)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a16, b16.T)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 10
+        out["context_torch_f16_matmul_TFLOPs"] = round(flops / (t * 1e-3) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(x_np, w_np)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

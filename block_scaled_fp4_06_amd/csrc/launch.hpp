@@ -1,0 +1,57 @@
+// launch.hpp -- internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Upper bound on the workgroups of the tensor-amax pass; each writes one partial.
+constexpr int kMaxAmaxParts = 4096;
+constexpr size_t kWorkspaceBytes = 64 * 1024;
+
+struct QuantLaunch {
+  const uint16_t *x;
+  int64_t rows, cols, ld;
+  int blocking;           // 0: 1x16, 1: 16x16
+  int rounding;           // 0: nearest-even, 1: stochastic
+  int rht;                // 1: RHT-16 along rows
+  uint32_t rht_k0, rht_k1; // RHT seed (Philox key of the sign vector)
+  uint32_t sr_k0, sr_k1;  // Philox key
+  uint64_t sr_base;       // Philox element index of x[0][0]
+  uint8_t *codes, *scales;
+  float *global_dec;
+  uint8_t *codes_t, *scales_t;
+  uint32_t *dev_status;
+  uint32_t *partials;     // workspace
+};
+
+hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
+
+struct DequantLaunch {
+  const uint8_t *codes, *scales;
+  const float *global_dec;
+  int64_t rows, cols, ld_y;
+  int blocking;
+  int out_f32;
+  void *y;
+};
+
+hipError_t launch_dequantize(const DequantLaunch &d, hipStream_t stream);
+
+struct GemmOperand {
+  const uint8_t *codes, *scales;
+  const float *global_dec;
+  int blocking;
+};
+
+struct GemmLaunch {
+  GemmOperand a, b;
+  int64_t M, N, K, ldc;
+  int out_f32;
+  void *c;
+};
+
+hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream);
+
+}  // namespace nvfp4

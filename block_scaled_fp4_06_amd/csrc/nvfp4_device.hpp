@@ -1,0 +1,168 @@
+// nvfp4_device.hpp -- device-side building blocks of the NVFP4 kernels (gfx950).
+//
+// Everything here is binary32 with round-to-nearest-even and is built with
+// -ffp-contract=off and without packed-FP32 instructions, so the results match a plain
+// IEEE evaluation in the same operation order bit for bit.  Division is the compiler's
+// correctly rounded fp32 division.
+//
+// Format sources: NVIDIA developer blog (zh-cn) "NVFP4 trains with precision of 16-bit
+// and speed and efficiency of 4-bit", section "用于预训练的 NVFP4 量化配方" (bullets:
+// 16-element micro-blocks, E4M3 scales, Hadamard transform, 2D blocks, stochastic
+// rounding); prism.simon-ai.net article 7890, section "MVFP4格式的核心架构革新" (FP32 tensor
+// scale above the E4M3 block scales).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr float kE2M1Max = 6.0f;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kTensorRange = 2688.0f;  // 6 * 448: top of both formats
+constexpr float kFltMax = 3.40282347e38f;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Unpack 16 bf16 values (two 16-byte words) to fp32 (exact).
+__device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float v[16]) {
+  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  v[8] = bf16_lo(b.x); v[9] = bf16_hi(b.x); v[10] = bf16_lo(b.y); v[11] = bf16_hi(b.y);
+  v[12] = bf16_lo(b.z); v[13] = bf16_hi(b.z); v[14] = bf16_lo(b.w); v[15] = bf16_hi(b.w);
+}
+
+// ---------------------------------------------------------------- RHT-16
+// y = 1/4 * H16 * diag(d) * x, Sylvester H16, with the sign vector d given as a 16-bit
+// mask (bit j set: d_j = -1).  Fixed evaluation order: sign flips (exact), butterfly
+// stages h = 1, 2, 4, 8 with (t_i, t_i+h) <- (t_i + t_i+h, t_i - t_i+h), then * 0.25.
+__device__ __forceinline__ void rht16(float v[16], uint32_t signmask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((signmask >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// ---------------------------------------------------------------- E4M3
+// Nearest-even E4M3FN code of s >= 0, saturating to 448 (code 0x7E); +inf -> 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s < kE4M3Max)) return 0x7Eu;
+  if (s < 0.015625f) {                       // below 2^-6: subnormal grid, step 2^-9
+    return (uint32_t)__builtin_rintf(s * 512.0f);  // 0..8 (8 is the smallest normal)
+  }
+  const int e = (int)(__float_as_uint(s) >> 23) - 127;                // -6 .. 8
+  const float t = s * __uint_as_float((uint32_t)(130 - e) << 23);    // s * 2^(3-e) in [8,16)
+  const uint32_t m = (uint32_t)__builtin_rintf(t);                   // 8 .. 16
+  return ((uint32_t)(e + 7) << 3) + (m - 8u);
+}
+
+// Value of an E4M3FN code 0..0x7E (block scales are never negative or NaN).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e == 0 ? (float)m * 0.001953125f
+                : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------- E2M1
+// Nearest-even magnitude code (0..7) of a >= 0; a >= 6 saturates to 7.
+__device__ __forceinline__ uint32_t e2m1_rn_mag(float a) {
+  if (a < 1.0f) return (uint32_t)__builtin_rintf(a + a);   // step 0.5: codes 0, 1, 2
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;   // keep 1 mantissa bit
+  const uint32_t c = r - 252u;                                     // 1.0 -> code 2
+  return c < 7u ? c : 7u;
+}
+
+// Stochastic magnitude code of a >= 0 with the 16-bit random integer k: round up iff
+// (k + 1/2) / 2^16 < (a - lo) / (hi - lo).  Both sides are exact in binary32.
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t k) {
+  if (!(a < kE2M1Max)) return 7u;
+  uint32_t lo_code;
+  float lo, inv_step;
+  if (a < 1.0f) {
+    lo_code = (uint32_t)(a + a);            // truncation: 0 or 1
+    lo = (float)lo_code * 0.5f;
+    inv_step = 2.0f;
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    lo = __uint_as_float(b & 0xFFC00000u);  // truncate to 1 mantissa bit
+    lo_code = (b >> 22) - 252u;
+    // step = 2^(e-1); 1/step = 2^(1-e): exponent field 254 - efield + 1 ... built directly
+    inv_step = __uint_as_float((254u - ((b >> 23) & 0xFFu) + 1u) << 23);
+  }
+  const float frac = (a - lo) * inv_step;
+  const float u = ((float)k + 0.5f) * 1.52587890625e-05f;  // 2^-16
+  return lo_code + (u < frac ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
+struct Philox4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{c0, c1, c2, c3};
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Max over the 16 lanes of a DPP row (lanes 16q .. 16q+15).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Tensor scales from the tensor amax bit pattern (|y| as uint; >= 0x7F800000: non-finite).
+struct TensorScale { float enc, dec; bool finite; };
+
+__device__ __forceinline__ TensorScale tensor_scale(uint32_t amax_bits) {
+  TensorScale t;
+  t.finite = amax_bits < 0x7F800000u;
+  const float amax = __uint_as_float(amax_bits);
+  if (!t.finite) {
+    t.enc = 1.0f;
+    t.dec = __uint_as_float(0x7FC00000u);
+  } else if (amax_bits == 0u) {
+    t.enc = 1.0f;
+    t.dec = 1.0f;
+  } else {
+    t.enc = fminf(kTensorRange / amax, kFltMax);
+    t.dec = amax / kTensorRange;
+  }
+  return t;
+}
+
+// Per-element multiplier of a block whose decoded E4M3 scale is sbd.
+__device__ __forceinline__ float block_mult(float s_enc, float sbd) {
+  return sbd == 0.0f ? 0.0f : fminf(s_enc / sbd, kFltMax);
+}
+
+}  // namespace nvfp4

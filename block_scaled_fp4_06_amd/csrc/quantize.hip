@@ -1,0 +1,286 @@
+// quantize.hip -- NVFP4 quantization kernels for gfx950.
+//
+// Recipe (NVIDIA developer blog zh-cn "NVFP4 trains with precision of 16-bit ...",
+// section "用于预训练的 NVFP4 量化配方"; prism.simon-ai.net article 7890, sections
+// "MVFP4格式的核心架构革新", "训练稳定性与敏感层保护策略", "应对异常值与舍入误差的技术手段"):
+// optional 16-point random Hadamard transform per 16-element row group, an FP32 tensor
+// scale from the tensor amax, an E4M3 scale per 1x16 or 16x16 block, E2M1 codes by
+// nearest-even or stochastic rounding (Philox4x32-10 keyed on (seed, element index)).
+//
+// The tensor scale needs the amax of the whole (transformed) tensor before any code can
+// be written, so quantization is two passes over the input:
+//   pass 1  amax_kernel: each workgroup reduces a contiguous range of row groups to one
+//           partial amax (integer max of |y| bit patterns: exact and order-free);
+//   pass 2  quant_1x16_kernel / quant_16x16_kernel: every workgroup reduces the partials,
+//           derives the tensor scales on the device (no host sync), and encodes its range.
+// Pass 2 re-reads an input that pass 1 has just streamed, which the 256 MB Infinity
+// Cache holds for the sizes this library targets.
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ uint32_t rht_signmask(uint32_t k0, uint32_t k1) {
+  // Sign vector: bit j of word 0 of Philox4x32-10(key = seed, counter = (0, 0, 1, 0)).
+  return philox4x32_10(0u, 0u, 1u, 0u, k0, k1).x & 0xFFFFu;
+}
+
+template <bool CONTIG>
+__device__ __forceinline__ const uint4 *group_ptr(const uint16_t *x, uint32_t g, uint32_t gpr,
+                                                  int64_t ld) {
+  if (CONTIG) return reinterpret_cast<const uint4 *>(x + (size_t)g * 16u);
+  const uint32_t r = g / gpr, gc = g - r * gpr;
+  return reinterpret_cast<const uint4 *>(x + (size_t)r * (size_t)ld + (size_t)gc * 16u);
+}
+
+__device__ __forceinline__ uint32_t block_max_bits(uint32_t m) {
+  __shared__ uint32_t red[kWaves];
+  m = wave_max_u32(m);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = max(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- pass 1
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restrict__ x,
+                                                        uint32_t ngroups, uint32_t gpr,
+                                                        int64_t ld, uint32_t rk0,
+                                                        uint32_t rk1, uint32_t per_wg,
+                                                        uint32_t *__restrict__ partials) {
+  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
+  const uint32_t begin = blockIdx.x * per_wg;
+  const uint32_t end = min(begin + per_wg, ngroups);
+  uint32_t m = 0;
+  for (uint32_t g = begin + threadIdx.x; g < end; g += kThreads) {
+    const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+    const uint4 a = p[0], b = p[1];
+    float v[16];
+    unpack16(a, b, v);
+    if (RHT) rht16(v, sm);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+  }
+  m = block_max_bits(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Reduce the partial maxima of pass 1 and publish the tensor scale (workgroup 0).
+__device__ __forceinline__ TensorScale finish_amax(const uint32_t *__restrict__ partials,
+                                                   uint32_t nparts, float *global_dec,
+                                                   uint32_t *dev_status) {
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partials[i]);
+  m = block_max_bits(m);
+  const TensorScale ts = tensor_scale(m);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *global_dec = ts.dec;
+    if (dev_status) *dev_status = ts.finite ? 0u : 1u;
+  }
+  return ts;
+}
+
+// Encode the 16 transformed values of one row group with the block multiplier rr.
+// k[16]: 16-bit random integers (stochastic rounding only).
+template <bool SR>
+__device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uint32_t k[16]) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float a = fabsf(y[j] * rr);
+    const uint32_t mag = SR ? e2m1_sr_mag(a, k[j]) : e2m1_rn_mag(a);
+    const uint32_t q = mag | ((__float_as_uint(y[j]) >> 28) & 8u);
+    if (j < 8) lo |= q << (4 * j);
+    else hi |= q << (4 * (j - 8));
+  }
+  return make_uint2(lo, hi);
+}
+
+// The 16 random integers of elements idx0 .. idx0+15 (idx0 a multiple of 16): element i
+// takes 16-bit lane (i & 7) of Philox4x32-10(key, counter = (i >> 3, 0, 0)).
+__device__ __forceinline__ void sr_draws(uint64_t idx0, uint32_t k0, uint32_t k1,
+                                         uint32_t k[16]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint64_t c = (idx0 >> 3) + (uint64_t)h;
+    const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, k0, k1);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k[8 * h + j] = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  }
+}
+
+__device__ __forceinline__ float absmax16(const float v[16]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+  return m;
+}
+
+// ---------------------------------------------------------------- pass 2, 1x16
+template <bool RHT, bool SR, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
+    const uint16_t *__restrict__ x, uint32_t ngroups, uint32_t gpr, int64_t ld, int64_t cols,
+    uint32_t rk0, uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base, uint32_t per_wg,
+    const uint32_t *__restrict__ partials, uint32_t nparts, uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ global_dec, uint32_t *dev_status) {
+  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
+  if (!ts.finite) return;
+  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
+  const uint32_t begin = blockIdx.x * per_wg;
+  const uint32_t end = min(begin + per_wg, ngroups);
+  for (uint32_t g = begin + threadIdx.x; g < end; g += kThreads) {
+    const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+    const uint4 a = p[0], b = p[1];
+    float v[16];
+    unpack16(a, b, v);
+    if (RHT) rht16(v, sm);
+    const float bmax = absmax16(v);
+    const uint32_t sb = e4m3_encode((bmax / kE2M1Max) * ts.enc);
+    const float rr = block_mult(ts.enc, e4m3_decode(sb));
+    uint32_t k[16];
+    if (SR) {
+      const uint32_t r = g / gpr, gc = g - r * gpr;
+      sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, k);
+    }
+    const uint2 q = encode16<SR>(v, rr, k);
+    reinterpret_cast<uint2 *>(codes)[g] = q;   // codes are contiguous: group g at 8*g
+    scales[g] = (uint8_t)sb;
+  }
+}
+
+// ---------------------------------------------------------------- pass 2, 16x16
+// 16 lanes per 16x16 tile (lane r holds row r of the tile); a workgroup covers 16 tiles
+// per step.  The tile amax is a max over the 16 lanes of a DPP row.  With TRANS the
+// codes of x^T are produced from the same registers through an LDS byte transpose.
+template <bool SR, bool TRANS>
+__global__ __launch_bounds__(kThreads) void quant_16x16_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sk0,
+    uint32_t sk1, uint64_t sr_base, const uint32_t *__restrict__ partials, uint32_t nparts,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
+    uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
+  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
+  if (!ts.finite) return;
+  __shared__ uint4 tbuf[16][16];
+  const uint32_t tpr = (uint32_t)(cols >> 4);          // tiles per tile-row
+  const uint32_t ntiles = (uint32_t)(rows >> 4) * tpr;
+  const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
+  for (uint32_t t0 = blockIdx.x * 16u; t0 < ntiles; t0 += gridDim.x * 16u) {
+    const uint32_t t = t0 + tl;
+    const bool valid = t < ntiles;
+    const uint32_t tr = valid ? t / tpr : 0u, tc = valid ? t - tr * tpr : 0u;
+    const int64_t row = (int64_t)tr * 16 + r;
+    float v[16];
+    if (valid) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(x + row * ld + (int64_t)tc * 16);
+      unpack16(p[0], p[1], v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
+    }
+    const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
+    const uint32_t sb = e4m3_encode((__uint_as_float(tmax) / kE2M1Max) * ts.enc);
+    const float rr = block_mult(ts.enc, e4m3_decode(sb));
+    uint32_t k[16];
+    if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
+    const uint2 q = encode16<SR>(v, rr, k);
+    if (valid) {
+      *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
+      if (r == 0) scales[t] = (uint8_t)sb;
+    }
+    if (TRANS) {
+      // one code per byte: byte j of tbuf[tl][r] = code of (row r, column j) of the tile
+      uint4 bytes;
+      uint32_t *bw = reinterpret_cast<uint32_t *>(&bytes);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t src = (w < 2) ? q.x : q.y;
+        const uint32_t sh = 16u * (w & 1);
+        bw[w] = ((src >> sh) & 0xFu) | (((src >> (sh + 4)) & 0xFu) << 8) |
+                (((src >> (sh + 8)) & 0xFu) << 16) | (((src >> (sh + 12)) & 0xFu) << 24);
+      }
+      tbuf[tl][r] = bytes;
+      __syncthreads();
+      // lane r now builds row r of the transposed tile: column r of this tile
+      const uint8_t *tb = reinterpret_cast<const uint8_t *>(&tbuf[tl][0]);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t c = tb[i * 16 + r];
+        if (i < 8) lo |= c << (4 * i);
+        else hi |= c << (4 * (i - 8));
+      }
+      if (valid) {
+        const int64_t trow = (int64_t)tc * 16 + r;  // row of x^T
+        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr * 8) =
+            make_uint2(lo, hi);
+        if (r == 0) scales_t[(size_t)tc * (size_t)(rows >> 4) + tr] = (uint8_t)sb;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
+  const uint64_t ngroups64 = (uint64_t)q.rows * (uint64_t)(q.cols / 16);
+  const uint32_t ngroups = (uint32_t)ngroups64;
+  const uint32_t gpr = (uint32_t)(q.cols / 16);
+  const bool contig = (q.ld == q.cols);
+  // pass 1 geometry: up to 1024 workgroups, each a contiguous range of row groups
+  uint32_t nparts = ceil_div(ngroups64 ? ngroups64 : 1, kThreads * 4);
+  if (nparts > 1024) nparts = 1024;
+  const uint32_t per_wg = ceil_div(ngroups64 ? ngroups64 : 1, nparts);
+  const bool rht = q.rht != 0;
+#define NVFP4_AMAX(R, C)                                                                    \
+  amax_kernel<R, C><<<nparts, kThreads, 0, stream>>>(q.x, ngroups, gpr, q.ld, q.rht_k0,    \
+                                                     q.rht_k1, per_wg, q.partials)
+  if (rht && contig) NVFP4_AMAX(true, true);
+  else if (rht) NVFP4_AMAX(true, false);
+  else if (contig) NVFP4_AMAX(false, true);
+  else NVFP4_AMAX(false, false);
+#undef NVFP4_AMAX
+
+  if (q.blocking == 0) {
+    const bool sr = q.rounding == 1;
+#define NVFP4_Q1(R, S, C)                                                                   \
+  quant_1x16_kernel<R, S, C><<<nparts, kThreads, 0, stream>>>(                              \
+      q.x, ngroups, gpr, q.ld, q.cols, q.rht_k0, q.rht_k1, q.sr_k0, q.sr_k1, q.sr_base,     \
+      per_wg, q.partials, nparts, q.codes, q.scales, q.global_dec, q.dev_status)
+    if (rht) {
+      if (sr) { if (contig) NVFP4_Q1(true, true, true); else NVFP4_Q1(true, true, false); }
+      else { if (contig) NVFP4_Q1(true, false, true); else NVFP4_Q1(true, false, false); }
+    } else {
+      if (sr) { if (contig) NVFP4_Q1(false, true, true); else NVFP4_Q1(false, true, false); }
+      else { if (contig) NVFP4_Q1(false, false, true); else NVFP4_Q1(false, false, false); }
+    }
+#undef NVFP4_Q1
+  } else {
+    const uint64_t ntiles = (uint64_t)(q.rows / 16) * (uint64_t)(q.cols / 16);
+    uint32_t grid = ceil_div(ntiles ? ntiles : 1, 16);
+    if (grid > 2048) grid = 2048;
+    const bool sr = q.rounding == 1, tr = q.codes_t != nullptr;
+#define NVFP4_Q16(S, T)                                                                     \
+  quant_16x16_kernel<S, T><<<grid, kThreads, 0, stream>>>(                                  \
+      q.x, q.rows, q.cols, q.ld, q.sr_k0, q.sr_k1, q.sr_base, q.partials, nparts, q.codes,  \
+      q.scales, q.codes_t, q.scales_t, q.global_dec, q.dev_status)
+    if (sr) { if (tr) NVFP4_Q16(true, true); else NVFP4_Q16(true, false); }
+    else { if (tr) NVFP4_Q16(false, true); else NVFP4_Q16(false, false); }
+#undef NVFP4_Q16
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

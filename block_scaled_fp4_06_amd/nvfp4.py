@@ -1,0 +1,207 @@
+"""ctypes binding of libnvfp4 (include/nvfp4.h).
+
+Argument marshalling only: every step of quantize, dequantize and the GEMM runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.  The
+library is loaded from this package directory; if it is missing or cannot be loaded the
+call raises -- there is no other implementation to fall back to.
+
+Low-level functions carry the C names (``nvfp4_quantize`` ...) and take raw pointers;
+``quantize`` / ``dequantize`` / ``gemm`` wrap them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+BLOCK_1x16, BLOCK_16x16 = 0, 1
+ROUND_RNE, ROUND_STOCHASTIC = 0, 1
+OUT_BF16, OUT_FP32 = 0, 1
+_BLOCKING = {"1x16": BLOCK_1x16, "16x16": BLOCK_16x16, 0: 0, 1: 1}
+_ROUNDING = {"rne": ROUND_RNE, "sr": ROUND_STOCHASTIC, "stochastic": ROUND_STOCHASTIC, 0: 0, 1: 1}
+
+
+class QuantParams(ctypes.Structure):
+    _fields_ = [("blocking", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("rht", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rht_seed", ctypes.c_uint64), ("sr_seed", ctypes.c_uint64),
+                ("sr_index_base", ctypes.c_uint64)]
+
+
+class Operand(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_dec", ctypes.c_void_p), ("blocking", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, nvfp4_status_string(status), status))
+
+
+EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
+            "nvfp4_gemm", "nvfp4_status_string", "nvfp4_abi_version")
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Open libnvfp4.so and declare the C signatures.  Raises if the library is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libnvfp4.so not built (expected at %s); run "
+                           "`python -m block_scaled_fp4_06_amd.build`" % path)
+    L = ctypes.CDLL(path)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.nvfp4_quantize_workspace_bytes.argtypes = []
+    L.nvfp4_quantize_workspace_bytes.restype = ctypes.c_size_t
+    L.nvfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(QuantParams), P, P, P, P, P,
+                                 P, P, ctypes.c_size_t, P]
+    L.nvfp4_quantize.restype = ctypes.c_int
+    L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, i64, i32, P]
+    L.nvfp4_dequantize.restype = ctypes.c_int
+    L.nvfp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
+                             P, i64, i32, P]
+    L.nvfp4_gemm.restype = ctypes.c_int
+    L.nvfp4_status_string.argtypes = [ctypes.c_int]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ C-named wrappers
+def nvfp4_quantize_workspace_bytes() -> int:
+    return int(load().nvfp4_quantize_workspace_bytes())
+
+
+def nvfp4_quantize(x, rows, cols, ld_x, params: QuantParams, codes, scales, global_dec,
+                   codes_t, scales_t, dev_status, workspace, workspace_bytes, stream) -> int:
+    return int(load().nvfp4_quantize(x, rows, cols, ld_x, ctypes.byref(params), codes, scales,
+                                     global_dec, codes_t, scales_t, dev_status, workspace,
+                                     workspace_bytes, stream))
+
+
+def nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y, ld_y, out_dtype,
+                     stream) -> int:
+    return int(load().nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y,
+                                       ld_y, out_dtype, stream))
+
+
+def nvfp4_gemm(a: Operand, b: Operand, M, N, K, c, ldc, out_dtype, stream) -> int:
+    return int(load().nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, c, ldc,
+                                 out_dtype, stream))
+
+
+def nvfp4_status_string(status: int) -> str:
+    return load().nvfp4_status_string(status).decode()
+
+
+def nvfp4_abi_version() -> int:
+    return int(load().nvfp4_abi_version())
+
+
+# ------------------------------------------------------------------ torch helpers
+@dataclass
+class NVFP4Tensor:
+    """Quantized tensor: codes (rows, cols//2) uint8, scales uint8, global_dec (1,) fp32."""
+    codes: "object"
+    scales: "object"
+    global_dec: "object"
+    rows: int
+    cols: int
+    blocking: int
+    codes_t: Optional[object] = None
+    scales_t: Optional[object] = None
+    status: Optional[object] = None
+
+    def transposed(self) -> "NVFP4Tensor":
+        """The W^T operand emitted alongside a 16x16 quantization (same tensor scale)."""
+        if self.codes_t is None:
+            raise ValueError("quantize(..., with_transpose=True) was not requested")
+        return NVFP4Tensor(self.codes_t, self.scales_t, self.global_dec, self.cols, self.rows,
+                           self.blocking)
+
+
+def _stream(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def quantize(x, blocking="1x16", rounding="rne", rht=False, rht_seed=0, sr_seed=0,
+             sr_index_base=0, with_transpose=False, stream=None, out=None) -> NVFP4Tensor:
+    """Quantize a 2-D bf16 CUDA tensor (row stride x.stride(0)) to NVFP4."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    rows, cols = x.shape
+    blk = _BLOCKING[blocking]
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        sshape = (rows // 16, cols // 16) if blk == BLOCK_16x16 else (rows, cols // 16)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        st = torch.empty(4, dtype=torch.int32, device=dev)
+        ct = st_ = None
+        if with_transpose:
+            ct = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+            st_ = torch.empty((cols // 16, rows // 16), dtype=torch.uint8, device=dev)
+        out = NVFP4Tensor(codes, scales, g, rows, cols, blk, ct, st_, st)
+    ws_bytes = nvfp4_quantize_workspace_bytes()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    prm = QuantParams(blk, _ROUNDING[rounding], 1 if rht else 0, 0, rht_seed, sr_seed,
+                      sr_index_base)
+    rc = nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), prm, _ptr(out.codes),
+                        _ptr(out.scales), _ptr(out.global_dec), _ptr(out.codes_t),
+                        _ptr(out.scales_t), _ptr(out.status), _ptr(ws), ws_bytes,
+                        _stream(stream, dev))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "nvfp4_quantize")
+    return out
+
+
+def dequantize(q: NVFP4Tensor, out_dtype=None, stream=None, out=None):
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    rc = nvfp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.global_dec), q.rows, q.cols,
+                          q.blocking, _ptr(out), out.stride(0), od,
+                          _stream(stream, q.codes.device))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "nvfp4_dequantize")
+    return out
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None):
+    """C = A . B^T with A (M x K) and B (N x K) NVFP4 operands."""
+    import torch
+    if a.cols != b.cols:
+        raise ValueError("K mismatch: %d vs %d" % (a.cols, b.cols))
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    oa = Operand(a.codes.data_ptr(), a.scales.data_ptr(), a.global_dec.data_ptr(), a.blocking, 0)
+    ob = Operand(b.codes.data_ptr(), b.scales.data_ptr(), b.global_dec.data_ptr(), b.blocking, 0)
+    rc = nvfp4_gemm(oa, ob, a.rows, b.rows, a.cols, _ptr(out), out.stride(0), od,
+                    _stream(stream, a.codes.device))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "nvfp4_gemm")
+    return out

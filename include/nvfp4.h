@@ -1,0 +1,167 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: NVFP4 block-scaled FP4 quantization for AMD MI355X (gfx950).
+ *
+ * The format and the recipe come from these pages (cited by page and section):
+ *   [NV-blog] developer.nvidia.com zh-cn blog "NVFP4 trains with precision of 16-bit and
+ *             speed and efficiency of 4-bit", section "用于预训练的 NVFP4 量化配方", five
+ *             bullets: 16-element micro-blocks, E4M3 block scales, Hadamard transform on
+ *             GEMM inputs, selective 2D block quantization, stochastic rounding.
+ *   [PR]      prism.simon-ai.net article 7890: section "MVFP4格式的核心架构革新" (an FP32
+ *             per-tensor scale on top of the E4M3 block scales), "训练稳定性与敏感层保护策略"
+ *             (16x16 blocks for weights so W and W^T agree), "应对异常值与舍入误差的技术手段"
+ *             (random Hadamard transform keeps norms; stochastic rounding of gradients).
+ *
+ * Conventions for every call:
+ *   - Pointers marked (device) are HIP device memory; (host) is host memory.  The caller
+ *     owns every buffer.  The library never allocates, never synchronizes and keeps no
+ *     global state: all calls are re-entrant and asynchronous on `stream`.
+ *   - Argument errors are returned before any HIP call is made.  A failed kernel launch
+ *     returns NVFP4_ERR_HIP.  Errors that depend on the data (inf/NaN input) are reported
+ *     on the device: the tensor scale becomes NaN and *dev_status becomes nonzero.
+ *   - Every device pointer must be 16-byte aligned; leading dimensions are in elements.
+ *   - Data pointers of an empty tensor (a zero dimension) may be NULL; the tensor scale
+ *     output of nvfp4_quantize is still written (1.0).
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *
+ * Storage (identical for inputs and outputs of all calls):
+ *   codes   packed E2M1, two per byte, row-major, rows x cols/2 bytes; column 2j in the
+ *           low nibble, column 2j+1 in the high nibble.  Nibble = sign<<3 | exp<<1 | man
+ *           (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   scales  E4M3 (OCP E4M3FN, max 448), row-major:
+ *             NVFP4_BLOCK_1x16 : rows    x cols/16 bytes (one per 16 consecutive elements
+ *                                of a row),
+ *             NVFP4_BLOCK_16x16: rows/16 x cols/16 bytes (one per 16x16 tile).
+ *   global  one float: the decode scale s_dec = amax / (6 * 448) of the (transformed)
+ *           tensor; 1.0 for an all-zero tensor; NaN if the input held inf or NaN.
+ *   A value decodes as e2m1(code) * e4m3(scale) * global.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+struct ihipStream_t;
+typedef struct ihipStream_t *nvfp4_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,       /* a size is negative or not a multiple of 16, or ld too small */
+    NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned or ld not a multiple of 8 */
+    NVFP4_ERR_UNSUPPORTED = 4, /* an option combination this version does not implement */
+    NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than nvfp4_quantize_workspace_bytes */
+    NVFP4_ERR_HIP = 6          /* a HIP launch failed */
+} nvfp4_status;
+
+typedef enum { NVFP4_BLOCK_1x16 = 0, NVFP4_BLOCK_16x16 = 1 } nvfp4_blocking;
+typedef enum { NVFP4_ROUND_RNE = 0, NVFP4_ROUND_STOCHASTIC = 1 } nvfp4_rounding;
+typedef enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_FP32 = 1 } nvfp4_out_dtype;
+
+/* Quantization options (host struct). */
+typedef struct {
+    int32_t blocking;       /* nvfp4_blocking: 1x16 for activations and gradients, 16x16
+                               for weights ([NV-blog] bullets 1 and 4; [PR] training
+                               stability section) */
+    int32_t rounding;       /* nvfp4_rounding: nearest-even, or stochastic ([NV-blog]
+                               bullet 5; [PR] outliers-and-rounding section) */
+    int32_t rht;            /* 1: apply the 16-point random Hadamard transform to every
+                               16-element row group before quantizing ([NV-blog] bullet 3);
+                               1x16 blocking only in this version */
+    int32_t reserved;       /* must be 0 */
+    uint64_t rht_seed;      /* selects the +-1 sign vector of the transform */
+    uint64_t sr_seed;       /* Philox4x32-10 key for stochastic rounding */
+    uint64_t sr_index_base; /* Philox element index of x[0][0]; a multiple of 16.  Lets a
+                               tensor be quantized in row chunks with the same draws as
+                               one call over the whole tensor */
+} nvfp4_quant_params;
+
+/* NVFP4 operand of the GEMM (device pointers): rows x K, K contiguous. */
+typedef struct {
+    const uint8_t *codes;     /* rows x K/2 bytes */
+    const uint8_t *scales;    /* E4M3 scales in the layout of `blocking` */
+    const float *global_dec;  /* 1 float (device) */
+    int32_t blocking;         /* nvfp4_blocking */
+    int32_t reserved;         /* must be 0 */
+} nvfp4_operand;
+
+/* Bytes of scratch memory nvfp4_quantize needs (device memory, caller-allocated, contents
+ * need no initialisation and are overwritten).  The same value for every shape. */
+size_t nvfp4_quantize_workspace_bytes(void);
+
+/*
+ * nvfp4_quantize -- quantize a row-major bf16 tensor to NVFP4.
+ *
+ * Computes, per [NV-blog] bullets 1-5 and [PR] "MVFP4格式的核心架构革新":
+ *   y      = x, or RHT16(x) along each 16-element row group (if p->rht);
+ *   amax   = max |y| over the tensor; s_enc = 2688 / amax; global = amax / 2688;
+ *   per block (1x16 or 16x16): sb = e4m3((max|y| / 6) * s_enc), nearest-even, at most 448;
+ *   per element: code = e2m1(y * (s_enc / e4m3_decode(sb))), nearest-even or stochastic
+ *   (Philox4x32-10 keyed on (sr_seed, element index)); the code keeps the sign of y.
+ *
+ * x           (device) bf16 bit patterns, rows x cols, row stride ld_x >= cols elements.
+ * rows, cols  multiples of 16 (0 is allowed and does nothing).
+ * p           (host) options; not retained.
+ * codes       (device, out) rows x cols/2 bytes.
+ * scales      (device, out) see Storage.
+ * global_dec  (device, out) 1 float.
+ * codes_t     (device, out, optional; 16x16 only) codes of x^T: cols x rows/2 bytes.  With
+ *             16x16 blocks these are exactly the transposed codes of x, so W and W^T come
+ *             from one read ([PR] training stability section).  NULL to skip.
+ * scales_t    (device, out) scales of x^T, cols/16 x rows/16; required iff codes_t is given.
+ * dev_status  (device, out, optional) 0, or 1 if the input held inf or NaN.
+ * workspace   (device) at least nvfp4_quantize_workspace_bytes() bytes.
+ */
+nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                            const nvfp4_quant_params *p, uint8_t *codes, uint8_t *scales,
+                            float *global_dec, uint8_t *codes_t, uint8_t *scales_t,
+                            uint32_t *dev_status, void *workspace, size_t workspace_bytes,
+                            nvfp4_stream_t stream);
+
+/*
+ * nvfp4_dequantize -- y = e2m1(code) * e4m3(scale) * global ([PR] "MVFP4与MXFP4": a 4-bit
+ * value times its block scale gives the real value; "MVFP4格式的核心架构革新": the FP32
+ * tensor scale on top).  The first product is exact; bf16 output rounds the fp32 value
+ * to nearest-even.
+ *
+ * codes, scales, global_dec  (device) as produced by nvfp4_quantize with `blocking`.
+ * y          (device, out) rows x cols, row stride ld_y >= cols elements (multiple of 8),
+ *            bf16 bit patterns or float per `out_dtype`.
+ */
+nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
+                              const float *global_dec, int64_t rows, int64_t cols,
+                              int32_t blocking, void *y, int64_t ld_y, int32_t out_dtype,
+                              nvfp4_stream_t stream);
+
+/*
+ * nvfp4_gemm -- C = A . B^T for NVFP4 operands, fp32 accumulation.
+ *
+ * The linear-layer matrix product the recipe accelerates ([NV-blog] recipe section,
+ * Figure 1 paragraph: LLMs rest on the matrix products of their linear layers).
+ *   C[m][n] = gA * gB * sum_k (e2m1 * e4m3)_A[m][k] * (e2m1 * e4m3)_B[n][k]
+ * a  (host struct, device pointers) M x K operand (activations; any blocking).
+ * b  (host struct, device pointers) N x K operand, i.e. the transposed weight W^T (with
+ *    16x16 blocks, the codes_t/scales_t of a K x N weight, or a weight quantized as N x K).
+ * M, N, K  multiples of 16.
+ * c  (device, out) M x N row-major, row stride ldc >= N (multiple of 8), bf16 or float.
+ */
+nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
+                        int64_t K, void *c, int64_t ldc, int32_t out_dtype,
+                        nvfp4_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *nvfp4_status_string(nvfp4_status s);
+
+/* NVFP4_ABI_VERSION of the built library. */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

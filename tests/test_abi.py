@@ -1,0 +1,135 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/nvfp4.h declares, and reject bad
+arguments with the documented status before it makes any HIP call -- so these calls
+use fake (but aligned) addresses and never reach a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_06_amd import nvfp4 as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any use
+ERR = dict(OK=0, NULL=1, SHAPE=2, ALIGN=3, UNSUPPORTED=4, WORKSPACE=5, HIP=6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(N.LIB_PATH):
+        from block_scaled_fp4_06_amd import build
+        build.build()
+    return N.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(N.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert N.nvfp4_abi_version() == 1
+    for s in range(7):
+        assert N.nvfp4_status_string(s)
+    assert "unknown" in N.nvfp4_status_string(99)
+    assert N.nvfp4_quantize_workspace_bytes() >= 4096
+
+
+def q(params=None, x=FAKE, rows=32, cols=32, ld=32, codes=FAKE, scales=FAKE, g=FAKE,
+      ct=None, st=None, status=None, ws=FAKE, wsb=None):
+    if params is None:
+        params = N.QuantParams(0, 0, 0, 0, 0, 0, 0)
+    if wsb is None:
+        wsb = N.nvfp4_quantize_workspace_bytes()
+    return N.nvfp4_quantize(x, rows, cols, ld, params, codes, scales, g, ct, st, status, ws,
+                            wsb, None)
+
+
+def test_quantize_argument_errors(lib):
+    P = N.QuantParams
+    assert q(x=None) == ERR["NULL"]
+    assert q(codes=None) == ERR["NULL"]
+    assert q(scales=None) == ERR["NULL"]
+    assert q(g=None) == ERR["NULL"]
+    assert q(rows=24) == ERR["SHAPE"]
+    assert q(cols=40, ld=40) == ERR["SHAPE"]
+    assert q(rows=-16) == ERR["SHAPE"]
+    assert q(ld=16) == ERR["SHAPE"]
+    assert q(ld=36) == ERR["ALIGN"]
+    assert q(x=FAKE + 8) == ERR["ALIGN"]
+    assert q(codes=FAKE + 4) == ERR["ALIGN"]
+    assert q(ws=None) == ERR["WORKSPACE"]
+    assert q(wsb=16) == ERR["WORKSPACE"]
+    assert q(P(2, 0, 0, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]
+    assert q(P(0, 3, 0, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]
+    assert q(P(0, 0, 2, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]
+    assert q(P(0, 0, 0, 1, 0, 0, 0)) == ERR["UNSUPPORTED"]
+    assert q(P(1, 0, 1, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]  # RHT with 16x16
+    assert q(P(0, 1, 0, 0, 0, 0, 8)) == ERR["SHAPE"]        # SR base not a multiple of 16
+    assert q(ct=FAKE) == ERR["NULL"]                         # codes_t without scales_t
+    assert q(ct=FAKE, st=FAKE) == ERR["UNSUPPORTED"]         # transpose needs 16x16
+    assert q(status=FAKE + 2) == ERR["ALIGN"]
+
+
+def test_quantize_null_params(lib):
+    L = lib
+    rc = L.nvfp4_quantize(FAKE, 16, 16, 16, None, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                          1 << 20, None)
+    assert rc == ERR["NULL"]
+
+
+def test_dequantize_argument_errors(lib):
+    def d(codes=FAKE, scales=FAKE, g=FAKE, rows=32, cols=32, blk=0, y=FAKE, ld=32, od=0):
+        return N.nvfp4_dequantize(codes, scales, g, rows, cols, blk, y, ld, od, None)
+    assert d(codes=None) == ERR["NULL"]
+    assert d(y=None) == ERR["NULL"]
+    assert d(g=None) == ERR["NULL"]
+    assert d(rows=8) == ERR["SHAPE"]
+    assert d(ld=16) == ERR["SHAPE"]
+    assert d(ld=44) == ERR["ALIGN"]
+    assert d(y=FAKE + 2) == ERR["ALIGN"]
+    assert d(blk=5) == ERR["UNSUPPORTED"]
+    assert d(od=2) == ERR["UNSUPPORTED"]
+    # an empty tensor is a no-op that needs no pointers (and makes no HIP call)
+    assert d(rows=0, codes=None, scales=None, g=None, y=None) == ERR["OK"]
+
+
+def test_gemm_argument_errors(lib):
+    def op(codes=FAKE, scales=FAKE, g=FAKE, blk=0, res=0):
+        return N.Operand(codes, scales, g, blk, res)
+
+    def gm(a=None, b=None, M=32, N_=32, K=64, c=FAKE, ldc=32, od=0):
+        a = a or op()
+        b = b or op(blk=1)
+        return N.nvfp4_gemm(a, b, M, N_, K, c, ldc, od, None)
+    assert lib.nvfp4_gemm(None, None, 16, 16, 16, FAKE, 16, 0, None) == ERR["NULL"]
+    assert gm(a=op(codes=None)) == ERR["NULL"]
+    assert gm(b=op(g=None)) == ERR["NULL"]
+    assert gm(c=None) == ERR["NULL"]
+    assert gm(K=40) == ERR["SHAPE"]
+    assert gm(M=-16) == ERR["SHAPE"]
+    assert gm(ldc=16) == ERR["SHAPE"]
+    assert gm(ldc=36) == ERR["ALIGN"]
+    assert gm(a=op(scales=FAKE + 1)) == ERR["ALIGN"]
+    assert gm(a=op(blk=7)) == ERR["UNSUPPORTED"]
+    assert gm(b=op(res=1)) == ERR["UNSUPPORTED"]
+    assert gm(od=9) == ERR["UNSUPPORTED"]
+    assert gm(M=0, a=op(codes=None, scales=None, g=None), c=None) == ERR["OK"]
+
+
+def test_python_wrapper_raises_when_library_missing(tmp_path, monkeypatch):
+    monkeypatch.setattr(N, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        N.load(str(tmp_path / "missing.so"))
