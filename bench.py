@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-micro", action="store_true")
     ap.add_argument("--context", action="store_true", help="also time torch fp16 matmul")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -233,6 +235,14 @@ def main():
                      "kernel": "gemm"},
         "kernels": kern,
     }
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+        del src, dst
     if not args.no_micro:
         log("standalone quantize workloads")
         out["quantize"] = micro_quantize(N, W)

@@ -17,17 +17,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float e2m1_value(uint32_t q) {
-  const uint32_t m = q & 7u;
-  const float mag = m < 2u ? (float)m * 0.5f
-                           : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-  return __uint_as_float(__float_as_uint(mag) | ((q & 8u) << 28));
-}
-
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Byte B of w holds two E2M1 codes (low nibble first): decode both to fp32 with the
+// hardware conversion (scale 1.0, exact), then (e2m1 * sbd) * s.
+template <int B>
+__device__ __forceinline__ void decode_byte(uint32_t w, float sbd, float s, float *v) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  v[0] = (f[0] * sbd) * s;   // first product exact
+  v[1] = (f[1] * sbd) * s;
 }
 
 template <bool F32, bool B16>
@@ -43,12 +45,14 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint32_t sidx = B16 ? (r >> 4) * gpr + gc : g;
     const float sbd = e4m3_decode(scales[sidx]);
     float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t q = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 0xFu;
-      const float e = e2m1_value(q) * sbd;   // exact
-      v[j] = e * s;
-    }
+    decode_byte<0>(cw.x, sbd, s, v + 0);
+    decode_byte<1>(cw.x, sbd, s, v + 2);
+    decode_byte<2>(cw.x, sbd, s, v + 4);
+    decode_byte<3>(cw.x, sbd, s, v + 6);
+    decode_byte<0>(cw.y, sbd, s, v + 8);
+    decode_byte<1>(cw.y, sbd, s, v + 10);
+    decode_byte<2>(cw.y, sbd, s, v + 12);
+    decode_byte<3>(cw.y, sbd, s, v + 14);
     const size_t off = (size_t)r * (size_t)ld_y + (size_t)gc * 16u;
     if (F32) {
       float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + off);

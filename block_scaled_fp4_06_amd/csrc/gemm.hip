@@ -190,6 +190,171 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tiles
+// Main path for K % 256 == 0.  One 256-thread workgroup per CU computes a 256 x 256 tile;
+// each wave owns 128 x 128 (4 x 4 MFMA blocks, 256 fp32 accumulators).  K advances 256
+// elements per step: every row of A and B contributes one 128-byte cache line of packed
+// codes and 16 scale bytes, which the direct global->LDS loads (global_load_lds_dwordx4)
+// bring into one of two LDS stages while the waves compute on the other.  The 16-byte
+// chunks of a row are stored at slot (chunk ^ (row & 7)) so the MFMA-operand reads of 8
+// consecutive rows hit 8 different bank groups.
+//
+// K mapping inside a step: lane half h reads chunk 2j + h (32 elements) for j = 0..3 and
+// feeds its 8-element pieces to four MFMAs; A and B use the same map.
+constexpr int kT2 = 256;                 // tile rows (M) and columns (N)
+constexpr int kRowB2 = 128;              // packed bytes per row per K step (256 elements)
+constexpr int kCodesB2 = kT2 * kRowB2;   // 32 KB per operand per stage
+constexpr int kScalesB2 = kT2 * 16;      // 4 KB per operand per stage
+constexpr int kStageB2 = 2 * kCodesB2 + 2 * kScalesB2;
+
+// 16 bytes per lane, global -> LDS; the LDS destination of lane l is l_base + 16 * l
+// (l_base must be wave-uniform).
+__device__ __forceinline__ void dma16(const void *g, uint8_t *l_base) {
+  __builtin_amdgcn_global_load_lds(g, l_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ half2_t scale_pair(uint32_t w, int h) {
+  // two E4M3 bytes (2h, 2h+1) of w -> two fp16 (exact)
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)(w >> (16 * h)), false);
+  half2_t r;
+  r[0] = (_Float16)f[0];
+  r[1] = (_Float16)f[1];
+  return r;
+}
+
+template <bool F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageB2];
+
+  // tile order: the workgroups that one XCD (block id % 8) runs form a contiguous
+  // range of tiles, walked four tile-rows at a time so concurrent tiles share A and B
+  const int G = tiles_m * tiles_n;
+  int b = blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int gm = 4;
+  const int band = b / (gm * tiles_n), in_band = b - band * gm * tiles_n;
+  const int rows_in_band = min(gm, tiles_m - band * gm);
+  const int tm = band * gm + in_band % rows_in_band;
+  const int tn = in_band / rows_in_band;
+  const int m0 = tm * kT2, n0 = tn * kT2;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t rowb = p.K >> 1;
+  const int kgroups = p.K >> 4;
+  const int nk = p.K / 256;
+
+  // DMA sources.  Instruction i of wave w fills LDS slots (8w + i) * 64 + lane, i.e.
+  // row 64w + 8i + lane/8, position lane%8, which holds chunk (lane%8) ^ (lane/8).
+  const int chunk = (lane & 7) ^ (lane >> 3);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 64 * wave + 8 * i + (lane >> 3);
+    aoff[i] = (uint32_t)(min(m0 + r, p.M - 1) * rowb + chunk * 16);
+    boff[i] = (uint32_t)(min(n0 + r, p.N - 1) * rowb + chunk * 16);
+  }
+  const int srow = 64 * wave + lane;   // scale rows: wave w loads rows 64w .. 64w+63
+  const int sra = min(m0 + srow, p.M - 1), srb = min(n0 + srow, p.N - 1);
+  const uint32_t asoff = (uint32_t)((p.a16 ? (sra >> 4) : sra) * kgroups);
+  const uint32_t bsoff = (uint32_t)((p.b16 ? (srb >> 4) : srb) * kgroups);
+
+  auto issue = [&](int kb, int stage) {
+    uint8_t *base = lds + stage * kStageB2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dma16(p.ac + aoff[i] + kb * kRowB2, base + (8 * wave + i) * 1024);
+      dma16(p.bc + boff[i] + kb * kRowB2, base + kCodesB2 + (8 * wave + i) * 1024);
+    }
+    dma16(p.as + asoff + kb * 16, base + 2 * kCodesB2 + wave * 1024);
+    dma16(p.bs + bsoff + kb * 16, base + 2 * kCodesB2 + kScalesB2 + wave * 1024);
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  issue(0, 0);
+  for (int kb = 0; kb < nk; ++kb) {
+    const int stage = kb & 1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into `stage` have landed
+    __syncthreads();                 // ... and every wave's; the other stage is free
+    if (kb + 1 < nk) issue(kb + 1, stage ^ 1);
+
+    const uint8_t *sa = lds + stage * kStageB2;
+    const uint8_t *sb = sa + kCodesB2;
+    const uint8_t *ssa = sa + 2 * kCodesB2;
+    const uint8_t *ssb = ssa + kScalesB2;
+    uint4 sca[4], scb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sca[i] = lds16(ssa + (wm * 128 + i * 32 + l32) * 16);
+      scb[i] = lds16(ssb + (wn * 128 + i * 32 + l32) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int slot = ((2 * j + h) ^ (l32 & 7)) * 16;
+      uint4 ca[4], cb[4];
+      half2_t hsa[4], hsb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ca[i] = lds16(sa + (wm * 128 + i * 32 + l32) * kRowB2 + slot);
+        cb[i] = lds16(sb + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
+        const uint32_t wa = j == 0 ? sca[i].x : j == 1 ? sca[i].y : j == 2 ? sca[i].z : sca[i].w;
+        const uint32_t wb = j == 0 ? scb[i].x : j == 1 ? scb[i].y : j == 2 ? scb[i].z : scb[i].w;
+        hsa[i] = scale_pair(wa, h);
+        hsb[i] = scale_pair(wb, h);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t ao[4], bo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wa = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
+          const uint32_t wb = s == 0 ? cb[i].x : s == 1 ? cb[i].y : s == 2 ? cb[i].z : cb[i].w;
+          ao[i] = dequant8<true>(wa, hsa[i][s >> 1]);
+          bo[i] = dequant8<true>(wb, hsb[i][s >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[i], bo[jj], acc[i][jj], 0, 0, 0);
+      }
+    }
+  }
+
+  const float alpha = (*p.ag) * (*p.bg);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int col = n0 + wn * 128 + jj * 32 + l32;
+        if (row < p.M && col < p.N) {
+          const float v = acc[i][jj][r] * alpha;
+          if (F32) {
+            reinterpret_cast<float *>(p.c)[(int64_t)row * p.ldc + col] = v;
+          } else {
+            const uint32_t u = __float_as_uint(v);
+            const uint32_t bb = ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u)
+                                                                 : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            reinterpret_cast<uint16_t *>(p.c)[(int64_t)row * p.ldc + col] = (uint16_t)bb;
+          }
+        }
+      }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
@@ -198,6 +363,12 @@ hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
   p.ac = g.a.codes; p.as = g.a.scales; p.ag = g.a.global_dec; p.a16 = g.a.blocking;
   p.bc = g.b.codes; p.bs = g.b.scales; p.bg = g.b.global_dec; p.b16 = g.b.blocking;
   p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K; p.ldc = g.ldc; p.c = g.c;
+  if (g.K > 0 && g.K % 256 == 0) {
+    const int tm = (int)((g.M + kT2 - 1) / kT2), tn = (int)((g.N + kT2 - 1) / kT2);
+    if (g.out_f32) gemm256_kernel<true><<<tm * tn, 256, 0, stream>>>(p, tm, tn);
+    else gemm256_kernel<false><<<tm * tn, 256, 0, stream>>>(p, tm, tn);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
   const bool k32 = (g.K % 32) == 0;
 #ifndef NVFP4_GEMM_HWCVT

@@ -108,6 +108,23 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t k) {
   return lo_code + (u < frac ? 1u : 0u);
 }
 
+// Nearest-even E2M1 codes of 16 values y[j] * rr, packed two per byte (element 2i in
+// the low nibble of byte i).  v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to
+// nearest-even, saturates to +-6 and keeps the sign (including -0), which is exactly the
+// encoder above; each instruction converts two values into one byte of the result.
+__device__ __forceinline__ uint2 e2m1_rn_pack16(const float y[16], float rr) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[0] * rr, y[1] * rr, 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[2] * rr, y[3] * rr, 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[4] * rr, y[5] * rr, 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[6] * rr, y[7] * rr, 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[8] * rr, y[9] * rr, 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[10] * rr, y[11] * rr, 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[12] * rr, y[13] * rr, 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[14] * rr, y[15] * rr, 1.0f, 3);
+  return make_uint2(lo, hi);
+}
+
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
 struct Philox4 { uint32_t x, y, z, w; };
@@ -116,8 +133,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
                                                   uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     k0 += 0x9E3779B9u;

@@ -61,14 +61,29 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restri
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
   uint32_t m = 0;
-  for (uint32_t g = begin + threadIdx.x; g < end; g += kThreads) {
-    const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
-    const uint4 a = p[0], b = p[1];
-    float v[16];
-    unpack16(a, b, v);
-    if (RHT) rht16(v, sm);
+  constexpr int U = 4;   // row groups in flight per thread
+  for (uint32_t g0 = begin + threadIdx.x; g0 < end; g0 += U * kThreads) {
+    uint4 a[U], b[U];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t g = g0 + u * kThreads;
+      if (g < end) {
+        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+        a[u] = p[0];
+        b[u] = p[1];
+      } else {
+        a[u] = make_uint4(0u, 0u, 0u, 0u);
+        b[u] = a[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[16];
+      unpack16(a[u], b[u], v);
+      if (RHT) rht16(v, sm);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+    }
   }
   m = block_max_bits(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -93,6 +108,7 @@ __device__ __forceinline__ TensorScale finish_amax(const uint32_t *__restrict__ 
 // k[16]: 16-bit random integers (stochastic rounding only).
 template <bool SR>
 __device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uint32_t k[16]) {
+  if (!SR) return e2m1_rn_pack16(y, rr);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -138,11 +154,24 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
-  for (uint32_t g = begin + threadIdx.x; g < end; g += kThreads) {
-    const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
-    const uint4 a = p[0], b = p[1];
+  constexpr int U = SR ? 1 : 2;   // row groups in flight per thread
+  for (uint32_t g0 = begin + threadIdx.x; g0 < end; g0 += U * kThreads) {
+    uint4 ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t g = g0 + u * kThreads;
+      if (g < end) {
+        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+        ra[u] = p[0];
+        rb[u] = p[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+    const uint32_t g = g0 + u * kThreads;
+    if (g >= end) break;
     float v[16];
-    unpack16(a, b, v);
+    unpack16(ra[u], rb[u], v);
     if (RHT) rht16(v, sm);
     const float bmax = absmax16(v);
     const uint32_t sb = e4m3_encode((bmax / kE2M1Max) * ts.enc);
@@ -155,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
     const uint2 q = encode16<SR>(v, rr, k);
     reinterpret_cast<uint2 *>(codes)[g] = q;   // codes are contiguous: group g at 8*g
     scales[g] = (uint8_t)sb;
+    }
   }
 }
 

@@ -275,7 +275,9 @@ def gemm_check(qa, qb, ref_a, ref_b, M, N_, K, rows=None):
 
 
 GEMM_SHAPES = [(128, 128, 64), (144, 208, 80), (256, 384, 320), (48, 16, 16), (16, 48, 528),
-               (400, 272, 1056)]
+               (400, 272, 1056),
+               # K % 256 == 0: the 256 x 256-tile kernel, with ragged M and N
+               (256, 256, 256), (400, 272, 1024), (48, 16, 512), (1040, 784, 2304)]
 
 
 @pytest.mark.parametrize("M,N_,K", GEMM_SHAPES)
