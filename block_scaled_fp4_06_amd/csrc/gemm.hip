@@ -207,21 +207,22 @@ constexpr int kCodesB2 = kT2 * kRowB2;   // 32 KB per operand per stage
 constexpr int kScalesB2 = kT2 * 16;      // 4 KB per operand per stage
 constexpr int kStageB2 = 2 * kCodesB2 + 2 * kScalesB2;
 
-// 16 bytes per lane, global -> LDS; the LDS destination of lane l is l_base + 16 * l
-// (l_base must be wave-uniform).
-__device__ __forceinline__ void dma16(const void *g, uint8_t *l_base) {
-  __builtin_amdgcn_global_load_lds(g, l_base, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at p (reads past the end return zero).  Every
+// field is made wave-uniform so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           0x00020000);
 }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 __device__ __forceinline__ half2_t scale_pair(uint32_t w, int h) {
-  // two E4M3 bytes (2h, 2h+1) of w -> two fp16 (exact)
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)(w >> (16 * h)), false);
-  half2_t r;
-  r[0] = (_Float16)f[0];
-  r[1] = (_Float16)f[1];
-  return r;
+  // two E4M3 bytes (2h, 2h+1) of w -> two fp16, exact (scale 1.0)
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * h), 1.0f, false);
 }
 
 template <bool F32>
@@ -248,30 +249,38 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   const int kgroups = p.K >> 4;
   const int nk = p.K / 256;
 
-  // DMA sources.  Instruction i of wave w fills LDS slots (8w + i) * 64 + lane, i.e.
-  // row 64w + 8i + lane/8, position lane%8, which holds chunk (lane%8) ^ (lane/8).
+  // DMA through bounds-checked buffer loads: a row past the end of an operand reads
+  // zeros (zero codes and zero scales contribute nothing; those rows are not stored).
+  // Instruction i of wave w fills LDS slots (8w + i) * 64 + lane, i.e. tile row
+  // 64w + 8i + lane/8, position lane%8, which holds chunk (lane%8) ^ (lane/8).
+  const int64_t srows_a = p.a16 ? (p.M + 15) / 16 : p.M, srows_b = p.b16 ? (p.N + 15) / 16 : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ac, (int64_t)p.M * rowb);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc, (int64_t)p.N * rowb);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as, srows_a * kgroups);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs, srows_b * kgroups);
   const int chunk = (lane & 7) ^ (lane >> 3);
-  uint32_t aoff[8], boff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 64 * wave + 8 * i + (lane >> 3);
-    aoff[i] = (uint32_t)(min(m0 + r, p.M - 1) * rowb + chunk * 16);
-    boff[i] = (uint32_t)(min(n0 + r, p.N - 1) * rowb + chunk * 16);
-  }
-  const int srow = 64 * wave + lane;   // scale rows: wave w loads rows 64w .. 64w+63
-  const int sra = min(m0 + srow, p.M - 1), srb = min(n0 + srow, p.N - 1);
-  const uint32_t asoff = (uint32_t)((p.a16 ? (sra >> 4) : sra) * kgroups);
-  const uint32_t bsoff = (uint32_t)((p.b16 ? (srb >> 4) : srb) * kgroups);
+  const uint32_t voff_code = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk * 16);
+  const int srow = 64 * wave + lane;   // scale rows: wave w loads tile rows 64w .. 64w+63
+  const uint32_t voff_sa = (uint32_t)((p.a16 ? (srow >> 4) : srow) * kgroups);
+  const uint32_t voff_sb = (uint32_t)((p.b16 ? (srow >> 4) : srow) * kgroups);
+  const uint32_t soff_sa0 = (uint32_t)((p.a16 ? (m0 >> 4) : m0) * kgroups);
+  const uint32_t soff_sb0 = (uint32_t)((p.b16 ? (n0 >> 4) : n0) * kgroups);
 
   auto issue = [&](int kb, int stage) {
     uint8_t *base = lds + stage * kStageB2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      dma16(p.ac + aoff[i] + kb * kRowB2, base + (8 * wave + i) * 1024);
-      dma16(p.bc + boff[i] + kb * kRowB2, base + kCodesB2 + (8 * wave + i) * 1024);
+      const uint32_t sa_off = __builtin_amdgcn_readfirstlane((uint32_t)((m0 + 8 * i) * rowb + kb * kRowB2));
+      const uint32_t sb_off = __builtin_amdgcn_readfirstlane((uint32_t)((n0 + 8 * i) * rowb + kb * kRowB2));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + (8 * wave + i) * 1024, 16, voff_code,
+                                               sa_off, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + kCodesB2 + (8 * wave + i) * 1024, 16,
+                                               voff_code, sb_off, 0, 0);
     }
-    dma16(p.as + asoff + kb * 16, base + 2 * kCodesB2 + wave * 1024);
-    dma16(p.bs + bsoff + kb * 16, base + 2 * kCodesB2 + kScalesB2 + wave * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, base + 2 * kCodesB2 + wave * 1024, 16, voff_sa,
+                                             __builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, base + 2 * kCodesB2 + kScalesB2 + wave * 1024, 16,
+                                             voff_sb, __builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16), 0, 0);
   };
 
   floatx16 acc[4][4];
@@ -282,52 +291,78 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  issue(0, 0);
-  for (int kb = 0; kb < nk; ++kb) {
-    const int stage = kb & 1;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into `stage` have landed
-    __syncthreads();                 // ... and every wave's; the other stage is free
-    if (kb + 1 < nk) issue(kb + 1, stage ^ 1);
-
-    const uint8_t *sa = lds + stage * kStageB2;
-    const uint8_t *sb = sa + kCodesB2;
-    const uint8_t *ssa = sa + 2 * kCodesB2;
-    const uint8_t *ssb = ssa + kScalesB2;
-    uint4 sca[4], scb[4];
+  // Software pipeline.  Within a K step, the operands of MFMA sub-step s+1 are read
+  // from LDS and dequantized while the 16 MFMAs of sub-step s run (scheduling barriers
+  // interleave one MFMA with a few VALU instructions).  Across K steps, the stage
+  // barrier sits after the last LDS read of the current stage (sub-step 11): past it,
+  // the loads of step kb+2 go into the freed stage and the first operands of step kb+1
+  // are prepared under the last MFMAs of step kb.
+  uint4 ca[2][4], cb[2][4];      // packed codes of two 32-element chunks (double buffer)
+  half2_t hsa[2][4], hsb[2][4];  // their block scales
+  half8_t ao[2][4], bo[2][4];    // dequantized operands of two sub-steps
+  // chunk j of a stage: 16 code bytes per block row and the two scale bytes (K groups
+  // 4j + 2h, 4j + 2h + 1) that cover them, into buffer j & 1
+  auto load_chunk16 = [&](const uint8_t *st, int j) {
+    const int slot = ((2 * j + h) ^ (l32 & 7)) * 16;
+    const uint8_t *ssa = st + 2 * kCodesB2, *ssb = ssa + kScalesB2;
+    const int b = j & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sca[i] = lds16(ssa + (wm * 128 + i * 32 + l32) * 16);
-      scb[i] = lds16(ssb + (wn * 128 + i * 32 + l32) * 16);
+      ca[b][i] = lds16(st + (wm * 128 + i * 32 + l32) * kRowB2 + slot);
+      cb[b][i] = lds16(st + kCodesB2 + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
+      const uint32_t wa = *reinterpret_cast<const uint32_t *>(ssa + (wm * 128 + i * 32 + l32) * 16 + 4 * j);
+      const uint32_t wb = *reinterpret_cast<const uint32_t *>(ssb + (wn * 128 + i * 32 + l32) * 16 + 4 * j);
+      hsa[b][i] = scale_pair(wa, h);
+      hsb[b][i] = scale_pair(wb, h);
     }
+  };
+  auto dequant_step = [&](int s, half8_t (&ad)[4], half8_t (&bd)[4]) {
+    const int q = s & 3, b = (s >> 2) & 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int slot = ((2 * j + h) ^ (l32 & 7)) * 16;
-      uint4 ca[4], cb[4];
-      half2_t hsa[4], hsb[4];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wa = q == 0 ? ca[b][i].x : q == 1 ? ca[b][i].y : q == 2 ? ca[b][i].z : ca[b][i].w;
+      const uint32_t wb = q == 0 ? cb[b][i].x : q == 1 ? cb[b][i].y : q == 2 ? cb[b][i].z : cb[b][i].w;
+      ad[i] = dequant8<true>(wa, hsa[b][i][q >> 1]);
+      bd[i] = dequant8<true>(wb, hsb[b][i][q >> 1]);
+    }
+  };
+
+  // Pipeline: chunk j of a K step is read from LDS four sub-steps before its first use;
+  // the operands of sub-step s+1 are dequantized under the MFMAs of sub-step s.  The
+  // stage barrier sits at sub-step 11, after the last LDS read of the current stage;
+  // past it the loads of step kb+2 go into the freed stage, chunk 0 of step kb+1 is read
+  // at sub-step 12 and its first operands prepared at sub-step 15.
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (nk > 1) issue(1, 1);
+  load_chunk16(lds, 0);
+  dequant_step(0, ao[0], bo[0]);
+  for (int kb = 0; kb < nk; ++kb) {
+    const uint8_t *st = lds + (kb & 1) * kStageB2;
+    const uint8_t *st_next = lds + ((kb + 1) & 1) * kStageB2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ca[i] = lds16(sa + (wm * 128 + i * 32 + l32) * kRowB2 + slot);
-        cb[i] = lds16(sb + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
-        const uint32_t wa = j == 0 ? sca[i].x : j == 1 ? sca[i].y : j == 2 ? sca[i].z : sca[i].w;
-        const uint32_t wb = j == 0 ? scb[i].x : j == 1 ? scb[i].y : j == 2 ? scb[i].z : scb[i].w;
-        hsa[i] = scale_pair(wa, h);
-        hsb[i] = scale_pair(wb, h);
+    for (int s = 0; s < 16; ++s) {
+      const int cur = s & 1;
+      if ((s & 3) == 0 && s < 12) load_chunk16(st, (s >> 2) + 1);
+      if (s == 11) {
+        __builtin_amdgcn_s_waitcnt(0);   // step kb+1 has landed; this wave is done with st
+        __syncthreads();
+        if (kb + 2 < nk) issue(kb + 2, kb & 1);
       }
+      if (s == 12 && kb + 1 < nk) load_chunk16(st_next, 0);
+      if (s + 1 < 16) dequant_step(s + 1, ao[cur ^ 1], bo[cur ^ 1]);
+      else if (kb + 1 < nk) dequant_step(0, ao[0], bo[0]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        half8_t ao[4], bo[4];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wa = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
-          const uint32_t wb = s == 0 ? cb[i].x : s == 1 ? cb[i].y : s == 2 ? cb[i].z : cb[i].w;
-          ao[i] = dequant8<true>(wa, hsa[i][s >> 1]);
-          bo[i] = dequant8<true>(wb, hsb[i][s >> 1]);
-        }
+        for (int jj = 0; jj < 4; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[cur][i], bo[cur][jj], acc[i][jj], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // LDS reads
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[i], bo[jj], acc[i][jj], 0, 0, 0);
+      for (int t = 0; t < 16; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0); // then up to five VALU
       }
     }
   }
