@@ -28,6 +28,7 @@ struct QuantLaunch {
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
 
+
 struct DequantLaunch {
   const uint8_t *codes, *scales;
   const float *global_dec;

@@ -151,11 +151,64 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// ---------------------------------------------------------------- lane exchange
+// Partner lane l ^ D inside a row of 16 lanes: DPP quad permutations for D = 1, 2, a row
+// rotation by 8 for D = 8 (the same as xor within 16 lanes) and ds_swizzle for D = 4.
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+}
+__device__ __forceinline__ uint32_t lane_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+}
+__device__ __forceinline__ uint32_t lane_xor4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);              // and 0x1F, xor 4
+}
+__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror 8
+}
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  return D == 1 ? lane_xor1(v) : D == 2 ? lane_xor2(v) : D == 4 ? lane_xor4(v) : lane_xor8(v);
+}
+
 // Max over the 16 lanes of a DPP row (lanes 16q .. 16q+15).
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  v = max(v, lane_xor1(v));
+  v = max(v, lane_xor2(v));
+  v = max(v, lane_xor4(v));
+  v = max(v, lane_xor8(v));
   return v;
+}
+
+// One butterfly stage of the 4-bit transpose, within each dword: a lane whose bit D is
+// clear keeps the nibbles at positions p with (p & D) == 0 and takes its partner's,
+// moved up by 4D bits; a lane with bit D set keeps the others and takes its partner's,
+// moved down.  The rotation leaves wrapped bits only where the mask discards them.
+template <int D>
+__device__ __forceinline__ uint32_t nibble_stage(uint32_t w, bool hi_lane) {
+  constexpr uint32_t s = 4 * D;
+  constexpr uint32_t m0 = D == 4 ? 0x0000FFFFu : D == 2 ? 0x00FF00FFu : 0x0F0F0F0Fu;
+  const uint32_t send = __builtin_amdgcn_alignbit(w, w, hi_lane ? 32 - s : s);  // rotate right
+  const uint32_t recv = lane_xor<D>(send);
+  const uint32_t keep = hi_lane ? ~m0 : m0;
+  return (w & keep) | (recv & ~keep);
+}
+
+// 16 x 16 transpose of 4-bit codes across the 16 lanes of a DPP row.  On entry lane r
+// holds row r (lo: columns 0..7, hi: columns 8..15, column c in nibble c % 8); on exit
+// lane r holds column r (rows 0..7 in lo, rows 8..15 in hi).  Four butterfly stages
+// swap bit D of the row index with bit D of the column index, D = 8, 4, 2, 1.
+__device__ __forceinline__ void transpose_nibbles16(uint32_t &lo, uint32_t &hi, uint32_t r) {
+  const bool b8 = r & 8;
+  const uint32_t recv = lane_xor8(b8 ? lo : hi);
+  lo = b8 ? recv : lo;
+  hi = b8 ? hi : recv;
+  lo = nibble_stage<4>(lo, r & 4);
+  hi = nibble_stage<4>(hi, r & 4);
+  lo = nibble_stage<2>(lo, r & 2);
+  hi = nibble_stage<2>(hi, r & 2);
+  lo = nibble_stage<1>(lo, r & 1);
+  hi = nibble_stage<1>(hi, r & 1);
 }
 
 // Tensor scales from the tensor amax bit pattern (|y| as uint; >= 0x7F800000: non-finite).

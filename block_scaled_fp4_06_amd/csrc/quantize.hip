@@ -143,35 +143,35 @@ __device__ __forceinline__ float absmax16(const float v[16]) {
 }
 
 // ---------------------------------------------------------------- pass 2, 1x16
+// One row group per thread per step; the next step's 32 input bytes are loaded before
+// the current group is encoded, so every wave keeps a load in flight while it computes.
 template <bool RHT, bool SR, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
     const uint16_t *__restrict__ x, uint32_t ngroups, uint32_t gpr, int64_t ld, int64_t cols,
     uint32_t rk0, uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base, uint32_t per_wg,
     const uint32_t *__restrict__ partials, uint32_t nparts, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_dec, uint32_t *dev_status) {
+  const uint32_t begin = blockIdx.x * per_wg;
+  const uint32_t end = min(begin + per_wg, ngroups);
+  uint32_t g = begin + threadIdx.x;
+  // the first group's load is in flight while the tensor scale is reduced (an empty
+  // tensor has no group to load: its workgroup only publishes the tensor scale)
+  uint4 ca = make_uint4(0u, 0u, 0u, 0u), cb = ca;
+  if (begin < end) {
+    const uint4 *p = group_ptr<CONTIG>(x, g < end ? g : begin, gpr, ld);
+    ca = p[0];
+    cb = p[1];
+  }
   const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
   if (!ts.finite) return;
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
-  const uint32_t begin = blockIdx.x * per_wg;
-  const uint32_t end = min(begin + per_wg, ngroups);
-  constexpr int U = SR ? 1 : 2;   // row groups in flight per thread
-  for (uint32_t g0 = begin + threadIdx.x; g0 < end; g0 += U * kThreads) {
-    uint4 ra[U], rb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t g = g0 + u * kThreads;
-      if (g < end) {
-        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
-        ra[u] = p[0];
-        rb[u] = p[1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-    const uint32_t g = g0 + u * kThreads;
-    if (g >= end) break;
+  for (; g < end; g += kThreads) {
+    // next group (on the last step this re-reads the current one: always a valid address)
+    const uint32_t gn = g + kThreads < end ? g + kThreads : g;
+    const uint4 *pn = group_ptr<CONTIG>(x, gn, gpr, ld);
+    const uint4 na = pn[0], nb = pn[1];
     float v[16];
-    unpack16(ra[u], rb[u], v);
+    unpack16(ca, cb, v);
     if (RHT) rht16(v, sm);
     const float bmax = absmax16(v);
     const uint32_t sb = e4m3_encode((bmax / kE2M1Max) * ts.enc);
@@ -181,86 +181,93 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
       const uint32_t r = g / gpr, gc = g - r * gpr;
       sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, k);
     }
-    const uint2 q = encode16<SR>(v, rr, k);
-    reinterpret_cast<uint2 *>(codes)[g] = q;   // codes are contiguous: group g at 8*g
+    reinterpret_cast<uint2 *>(codes)[g] = encode16<SR>(v, rr, k);  // group g at byte 8g
     scales[g] = (uint8_t)sb;
-    }
+    ca = na;
+    cb = nb;
   }
 }
 
 // ---------------------------------------------------------------- pass 2, 16x16
 // 16 lanes per 16x16 tile (lane r holds row r of the tile); a workgroup covers 16 tiles
-// per step.  The tile amax is a max over the 16 lanes of a DPP row.  With TRANS the
-// codes of x^T are produced from the same registers through an LDS byte transpose.
+// per step.  The tile amax is a DPP max over the 16 lanes of a row; with TRANS the codes
+// of x^T come from the same registers through an in-register 4-bit transpose.
 template <bool SR, bool TRANS>
 __global__ __launch_bounds__(kThreads) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sk0,
     uint32_t sk1, uint64_t sr_base, const uint32_t *__restrict__ partials, uint32_t nparts,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
     uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
-  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
-  if (!ts.finite) return;
-  __shared__ uint4 tbuf[16][16];
   const uint32_t tpr = (uint32_t)(cols >> 4);          // tiles per tile-row
   const uint32_t ntiles = (uint32_t)(rows >> 4) * tpr;
   const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
-  for (uint32_t t0 = blockIdx.x * 16u; t0 < ntiles; t0 += gridDim.x * 16u) {
+  const uint32_t stride = gridDim.x * 16u;
+  // every lane loads a valid address (tile 0 when past the end) and masks the data, so
+  // the 16 lanes of a tile always run the reductions together
+  auto load = [&](uint32_t t, uint4 &a, uint4 &b) {
+    if (ntiles == 0) {   // empty tensor: nothing to read
+      a = make_uint4(0u, 0u, 0u, 0u);
+      b = a;
+      return;
+    }
+    const bool valid = t < ntiles;
+    const uint32_t tt = valid ? t : 0u;
+    const uint32_t tr = tt / tpr, tc = tt - tr * tpr;
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + ((int64_t)tr * 16 + r) * ld + (int64_t)tc * 16);
+    const uint4 ra = p[0], rb = p[1];
+    const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
+    a = make_uint4(ra.x & m, ra.y & m, ra.z & m, ra.w & m);
+    b = make_uint4(rb.x & m, rb.y & m, rb.z & m, rb.w & m);
+  };
+  uint32_t t0 = blockIdx.x * 16u;
+  uint4 ca, cb;
+  load(t0 + tl, ca, cb);              // in flight while the tensor scale is reduced
+  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
+  if (!ts.finite) return;
+  for (; t0 < ntiles; t0 += stride) {
+    uint4 na, nb;
+    load(t0 + stride + tl, na, nb);   // past the end: masked re-read of tile 0
     const uint32_t t = t0 + tl;
     const bool valid = t < ntiles;
     const uint32_t tr = valid ? t / tpr : 0u, tc = valid ? t - tr * tpr : 0u;
     const int64_t row = (int64_t)tr * 16 + r;
     float v[16];
-    if (valid) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(x + row * ld + (int64_t)tc * 16);
-      unpack16(p[0], p[1], v);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
-    }
+    unpack16(ca, cb, v);
     const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
     const uint32_t sb = e4m3_encode((__uint_as_float(tmax) / kE2M1Max) * ts.enc);
     const float rr = block_mult(ts.enc, e4m3_decode(sb));
     uint32_t k[16];
     if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
-    const uint2 q = encode16<SR>(v, rr, k);
+    uint2 q = encode16<SR>(v, rr, k);
     if (valid) {
       *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
       if (r == 0) scales[t] = (uint8_t)sb;
     }
     if (TRANS) {
-      // one code per byte: byte j of tbuf[tl][r] = code of (row r, column j) of the tile
-      uint4 bytes;
-      uint32_t *bw = reinterpret_cast<uint32_t *>(&bytes);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t src = (w < 2) ? q.x : q.y;
-        const uint32_t sh = 16u * (w & 1);
-        bw[w] = ((src >> sh) & 0xFu) | (((src >> (sh + 4)) & 0xFu) << 8) |
-                (((src >> (sh + 8)) & 0xFu) << 16) | (((src >> (sh + 12)) & 0xFu) << 24);
-      }
-      tbuf[tl][r] = bytes;
-      __syncthreads();
-      // lane r now builds row r of the transposed tile: column r of this tile
-      const uint8_t *tb = reinterpret_cast<const uint8_t *>(&tbuf[tl][0]);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t c = tb[i * 16 + r];
-        if (i < 8) lo |= c << (4 * i);
-        else hi |= c << (4 * (i - 8));
-      }
+      transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
       if (valid) {
         const int64_t trow = (int64_t)tc * 16 + r;  // row of x^T
-        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr * 8) =
-            make_uint2(lo, hi);
+        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr * 8) = q;
         if (r == 0) scales_t[(size_t)tc * (size_t)(rows >> 4) + tr] = (uint8_t)sb;
       }
-      __syncthreads();
     }
+    ca = na;
+    cb = nb;
   }
 }
 
 uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// Workgroup caps of the encode pass (8 resident 256-thread workgroups per CU).
+#ifndef NVFP4_Q1_MAX_WG
+#define NVFP4_Q1_MAX_WG 2048
+#endif
+#ifndef NVFP4_Q16_MAX_WG
+#define NVFP4_Q16_MAX_WG 2048
+#endif
+#ifndef NVFP4_AMAX_MAX_WG
+#define NVFP4_AMAX_MAX_WG 1024
+#endif
 
 }  // namespace
 
@@ -271,7 +278,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
   const bool contig = (q.ld == q.cols);
   // pass 1 geometry: up to 1024 workgroups, each a contiguous range of row groups
   uint32_t nparts = ceil_div(ngroups64 ? ngroups64 : 1, kThreads * 4);
-  if (nparts > 1024) nparts = 1024;
+  if (nparts > NVFP4_AMAX_MAX_WG) nparts = NVFP4_AMAX_MAX_WG;
   const uint32_t per_wg = ceil_div(ngroups64 ? ngroups64 : 1, nparts);
   const bool rht = q.rht != 0;
 #define NVFP4_AMAX(R, C)                                                                    \
@@ -285,10 +292,15 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
 
   if (q.blocking == 0) {
     const bool sr = q.rounding == 1;
+    // pass 2 grid: enough workgroups for 8 per CU, each a contiguous range of groups
+    uint32_t grid2 = ceil_div(ngroups64 ? ngroups64 : 1, kThreads);
+    if (grid2 > NVFP4_Q1_MAX_WG) grid2 = NVFP4_Q1_MAX_WG;
+    const uint32_t per_wg2 = ceil_div(ngroups64 ? ngroups64 : 1, grid2);
+    grid2 = ceil_div(ngroups64 ? ngroups64 : 1, per_wg2);
 #define NVFP4_Q1(R, S, C)                                                                   \
-  quant_1x16_kernel<R, S, C><<<nparts, kThreads, 0, stream>>>(                              \
+  quant_1x16_kernel<R, S, C><<<grid2, kThreads, 0, stream>>>(                               \
       q.x, ngroups, gpr, q.ld, q.cols, q.rht_k0, q.rht_k1, q.sr_k0, q.sr_k1, q.sr_base,     \
-      per_wg, q.partials, nparts, q.codes, q.scales, q.global_dec, q.dev_status)
+      per_wg2, q.partials, nparts, q.codes, q.scales, q.global_dec, q.dev_status)
     if (rht) {
       if (sr) { if (contig) NVFP4_Q1(true, true, true); else NVFP4_Q1(true, true, false); }
       else { if (contig) NVFP4_Q1(true, false, true); else NVFP4_Q1(true, false, false); }
@@ -300,7 +312,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
   } else {
     const uint64_t ntiles = (uint64_t)(q.rows / 16) * (uint64_t)(q.cols / 16);
     uint32_t grid = ceil_div(ntiles ? ntiles : 1, 16);
-    if (grid > 2048) grid = 2048;
+    if (grid > NVFP4_Q16_MAX_WG) grid = NVFP4_Q16_MAX_WG;
     const bool sr = q.rounding == 1, tr = q.codes_t != nullptr;
 #define NVFP4_Q16(S, T)                                                                     \
   quant_16x16_kernel<S, T><<<grid, kThreads, 0, stream>>>(                                  \
