@@ -46,6 +46,22 @@ def dequant_bytes(rows, cols, blocking, out_bytes=2):
     return n // 2 + sc + 4 + n * out_bytes
 
 
+def gemm_traffic_bytes():
+    """HBM bytes of one GEMM launch measured with rocprofv3 (FETCH_SIZE x2, WRITE_SIZE x1,
+    scales from a plain-copy calibration), or None when the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    rec_path = os.path.join(here, "profiles", "gemm_w5_traffic.json")
+    src_path = os.path.join(here, "block_scaled_fp4_06_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(rec_path))
+        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return int(rec["traffic_bytes"]) if rec.get("source_sha256") == src else None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,8 +247,8 @@ def main():
                                "8192x20480x5120 (fp32 acc, bf16 out) + dequantize X",
                    "M": M, "N": NN, "K": K},
         "roofline": {"bound": "mfma", "achieved": g["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": g["frac_mfma_f16"], "traffic": None,
-                     "kernel": "gemm"},
+                     "unit": "TFLOP/s", "frac": g["frac_mfma_f16"],
+                     "traffic": gemm_traffic_bytes(), "kernel": "gemm"},
         "kernels": kern,
     }
     if args.copy_calibration:
