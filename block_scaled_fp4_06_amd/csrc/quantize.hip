@@ -189,47 +189,55 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
 }
 
 // ---------------------------------------------------------------- pass 2, 16x16
-// 16 lanes per 16x16 tile (lane r holds row r of the tile); a workgroup covers 16 tiles
-// per step.  The tile amax is a DPP max over the 16 lanes of a row; with TRANS the codes
-// of x^T come from the same registers through an in-register 4-bit transpose.
+// A workgroup encodes a block of 16 x 16 tiles (256 x 256 elements) in 16 steps, one
+// tile-row of 16 tiles per step; 16 lanes of a DPP row hold the 16 rows of a tile.  The
+// tile amax is a DPP max over the row.  Codes of x are stored per step (128 contiguous
+// bytes per row); with TRANS the codes of x^T come from an in-register 4-bit transpose and
+// are assembled in LDS so that each of the block's 256 rows of x^T is written as one
+// 128-byte line at the end (a row of x^T receives 8 bytes per tile-row of x).
+constexpr int kTStride = 136;   // LDS bytes per staged x^T row (128 + 8 against bank conflicts)
+
 template <bool SR, bool TRANS>
 __global__ __launch_bounds__(kThreads) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sk0,
     uint32_t sk1, uint64_t sr_base, const uint32_t *__restrict__ partials, uint32_t nparts,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
     uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTStride : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 256 : 16];
   const uint32_t tpr = (uint32_t)(cols >> 4);          // tiles per tile-row
-  const uint32_t ntiles = (uint32_t)(rows >> 4) * tpr;
+  const uint32_t tpc = (uint32_t)(rows >> 4);          // tiles per tile-column
+  if (tpr == 0 || tpc == 0) {   // empty tensor: only the tensor scale is written
+    finish_amax(partials, nparts, global_dec, dev_status);
+    return;
+  }
+  const uint32_t bpr = (tpr + 15) >> 4;                // blocks per block-row
+  const uint32_t blk = blockIdx.x;
+  const uint32_t br = blk / bpr, bc = blk - br * bpr;
   const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
-  const uint32_t stride = gridDim.x * 16u;
-  // every lane loads a valid address (tile 0 when past the end) and masks the data, so
-  // the 16 lanes of a tile always run the reductions together
-  auto load = [&](uint32_t t, uint4 &a, uint4 &b) {
-    if (ntiles == 0) {   // empty tensor: nothing to read
-      a = make_uint4(0u, 0u, 0u, 0u);
-      b = a;
-      return;
-    }
-    const bool valid = t < ntiles;
-    const uint32_t tt = valid ? t : 0u;
-    const uint32_t tr = tt / tpr, tc = tt - tr * tpr;
-    const uint4 *p = reinterpret_cast<const uint4 *>(x + ((int64_t)tr * 16 + r) * ld + (int64_t)tc * 16);
+  const uint32_t tc = bc * 16 + tl;                    // this lane's tile column
+  const bool col_ok = tc < tpr;
+  // every lane loads a valid address (the block's first tile when past an edge) and
+  // masks the data, so the 16 lanes of a tile always run the reductions together
+  auto load = [&](uint32_t it, uint4 &a, uint4 &b) {
+    const uint32_t tr = br * 16 + it;
+    const bool valid = col_ok && tr < tpc;
+    const uint32_t rr_ = valid ? tr : br * 16, cc = valid ? tc : bc * 16;
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + ((int64_t)rr_ * 16 + r) * ld + (int64_t)cc * 16);
     const uint4 ra = p[0], rb = p[1];
     const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
     a = make_uint4(ra.x & m, ra.y & m, ra.z & m, ra.w & m);
     b = make_uint4(rb.x & m, rb.y & m, rb.z & m, rb.w & m);
   };
-  uint32_t t0 = blockIdx.x * 16u;
   uint4 ca, cb;
-  load(t0 + tl, ca, cb);              // in flight while the tensor scale is reduced
+  load(0, ca, cb);                    // in flight while the tensor scale is reduced
   const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
   if (!ts.finite) return;
-  for (; t0 < ntiles; t0 += stride) {
+  const uint32_t nit = min(16u, tpc - br * 16);
+  for (uint32_t it = 0; it < nit; ++it) {
     uint4 na, nb;
-    load(t0 + stride + tl, na, nb);   // past the end: masked re-read of tile 0
-    const uint32_t t = t0 + tl;
-    const bool valid = t < ntiles;
-    const uint32_t tr = valid ? t / tpr : 0u, tc = valid ? t - tr * tpr : 0u;
+    load(it + 1 < nit ? it + 1 : it, na, nb);
+    const uint32_t tr = br * 16 + it;
     const int64_t row = (int64_t)tr * 16 + r;
     float v[16];
     unpack16(ca, cb, v);
@@ -239,20 +247,38 @@ __global__ __launch_bounds__(kThreads) void quant_16x16_kernel(
     uint32_t k[16];
     if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
     uint2 q = encode16<SR>(v, rr, k);
-    if (valid) {
+    if (col_ok) {
       *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
-      if (r == 0) scales[t] = (uint8_t)sb;
+      if (r == 0) scales[(size_t)tr * tpr + tc] = (uint8_t)sb;
     }
     if (TRANS) {
       transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
-      if (valid) {
-        const int64_t trow = (int64_t)tc * 16 + r;  // row of x^T
-        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr * 8) = q;
-        if (r == 0) scales_t[(size_t)tc * (size_t)(rows >> 4) + tr] = (uint8_t)sb;
-      }
+      *reinterpret_cast<uint2 *>(tbuf + (tl * 16 + r) * kTStride + it * 8) = q;
+      if (r == 0) sbuf[tl * 16 + it] = (uint8_t)sb;
     }
     ca = na;
     cb = nb;
+  }
+  if (TRANS) {
+    __syncthreads();
+    // 256 staged rows of x^T, nit * 8 bytes each: row j of the block is x^T row
+    // bc*256 + j, bytes [br*128, br*128 + 8*nit)
+    const uint32_t nbytes = nit * 8;
+    for (uint32_t i = threadIdx.x; i < 256 * 16; i += kThreads) {
+      const uint32_t j = i >> 4, c8 = i & 15u;     // row, 8-byte chunk
+      const uint32_t ttc = bc * 16 + (j >> 4);
+      if (ttc < tpr && c8 * 8 < nbytes) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTStride + c8 * 8);
+        const int64_t trow = (int64_t)bc * 256 + j;
+        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)br * 128 + c8 * 8) = w;
+      }
+    }
+    // scales of x^T: row tc (one per tile column), bytes [br*16, br*16 + nit)
+    if (threadIdx.x < 256) {
+      const uint32_t tcl = threadIdx.x >> 4, it = threadIdx.x & 15u;
+      const uint32_t ttc = bc * 16 + tcl;
+      if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + br * 16 + it] = sbuf[tcl * 16 + it];
+    }
   }
 }
 
@@ -261,9 +287,6 @@ uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); 
 // Workgroup caps of the encode pass (8 resident 256-thread workgroups per CU).
 #ifndef NVFP4_Q1_MAX_WG
 #define NVFP4_Q1_MAX_WG 2048
-#endif
-#ifndef NVFP4_Q16_MAX_WG
-#define NVFP4_Q16_MAX_WG 2048
 #endif
 #ifndef NVFP4_AMAX_MAX_WG
 #define NVFP4_AMAX_MAX_WG 1024
@@ -310,9 +333,9 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
     }
 #undef NVFP4_Q1
   } else {
-    const uint64_t ntiles = (uint64_t)(q.rows / 16) * (uint64_t)(q.cols / 16);
-    uint32_t grid = ceil_div(ntiles ? ntiles : 1, 16);
-    if (grid > NVFP4_Q16_MAX_WG) grid = NVFP4_Q16_MAX_WG;
+    // one workgroup per block of 16 x 16 tiles
+    uint32_t grid = (uint32_t)(((q.rows / 16 + 15) / 16) * ((q.cols / 16 + 15) / 16));
+    if (grid == 0) grid = 1;   // an empty tensor still publishes its tensor scale
     const bool sr = q.rounding == 1, tr = q.codes_t != nullptr;
 #define NVFP4_Q16(S, T)                                                                     \
   quant_16x16_kernel<S, T><<<grid, kThreads, 0, stream>>>(                                  \
