@@ -44,6 +44,9 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
   const bool empty = rows == 0 || cols == 0;  // data pointers of empty tensors may be NULL
   if (!global_dec || (!empty && (!x || !codes || !scales))) return NVFP4_ERR_NULL;
   if (!workspace || workspace_bytes < nvfp4::kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+  if (nvfp4::kCoordBytes + 8 * nvfp4::quantize_chunks(rows, cols, p->blocking, p->rounding) >
+      workspace_bytes)
+    return NVFP4_ERR_WORKSPACE;
   if ((ld_x & 7) || !aligned16(x) || !aligned16(codes) || !aligned16(scales) ||
       !aligned16(global_dec) || !aligned16(workspace) || (codes_t && !aligned16(codes_t)) ||
       (scales_t && !aligned16(scales_t)) || (dev_status && !aligned16(dev_status)))
@@ -68,7 +71,7 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
   q.codes_t = codes_t;
   q.scales_t = scales_t;
   q.dev_status = dev_status;
-  q.partials = static_cast<uint32_t *>(workspace);
+  q.ws = workspace;
   return from_hip(nvfp4::launch_quantize(q, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -6,9 +6,13 @@
 
 namespace nvfp4 {
 
-// Upper bound on the workgroups of the tensor-amax pass; each writes one partial.
-constexpr int kMaxAmaxParts = 4096;
-constexpr size_t kWorkspaceBytes = 64 * 1024;
+// Quantization workspace: a block of coordination words, then one 64-bit word per chunk of
+// the input (see quantize.hip).  8 MiB covers the largest tensor the ABI accepts.
+constexpr size_t kCoordBytes = 8192;
+constexpr size_t kWorkspaceBytes = ((size_t)8 << 20) + kCoordBytes;
+
+// Chunks the quantization kernel divides a rows x cols tensor into.
+uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding);
 
 struct QuantLaunch {
   const uint16_t *x;
@@ -23,7 +27,7 @@ struct QuantLaunch {
   float *global_dec;
   uint8_t *codes_t, *scales_t;
   uint32_t *dev_status;
-  uint32_t *partials;     // workspace
+  void *ws;               // workspace (kCoordBytes + 8 bytes per chunk), zero-filled once
 };
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);

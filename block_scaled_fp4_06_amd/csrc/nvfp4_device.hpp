@@ -38,42 +38,77 @@ __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float v
 // y = 1/4 * H16 * diag(d) * x, Sylvester H16, with the sign vector d given as a 16-bit
 // mask (bit j set: d_j = -1).  Fixed evaluation order: sign flips (exact), butterfly
 // stages h = 1, 2, 4, 8 with (t_i, t_i+h) <- (t_i + t_i+h, t_i - t_i+h), then * 0.25.
-__device__ __forceinline__ void rht16(float v[16], uint32_t signmask) {
+// rht16_unscaled stops before the final quarter; rht16 applies it.
+__device__ __forceinline__ void rht16_stage(float v[16], int h) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i & h) continue;
+    const float a = v[i], b = v[i + h];
+    v[i] = a + b;
+    v[i + h] = a - b;
+  }
+}
+
+__device__ __forceinline__ void rht16_signs(float v[16], uint32_t signmask) {
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((signmask >> j) & 1u) << 31));
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i & h) continue;
-      const float a = v[i], b = v[i + h];
-      v[i] = a + b;
-      v[i + h] = a - b;
-    }
-  }
+}
+
+__device__ __forceinline__ void rht16_unscaled(float v[16], uint32_t signmask) {
+  rht16_signs(v, signmask);
+  rht16_stage(v, 1);
+  rht16_stage(v, 2);
+  rht16_stage(v, 4);
+  rht16_stage(v, 8);
+}
+
+__device__ __forceinline__ void rht16(float v[16], uint32_t signmask) {
+  rht16_unscaled(v, signmask);
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
 }
 
-// ---------------------------------------------------------------- E4M3
-// Nearest-even E4M3FN code of s >= 0, saturating to 448 (code 0x7E); +inf -> 0x7E.
-__device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (!(s < kE4M3Max)) return 0x7Eu;
-  if (s < 0.015625f) {                       // below 2^-6: subnormal grid, step 2^-9
-    return (uint32_t)__builtin_rintf(s * 512.0f);  // 0..8 (8 is the smallest normal)
-  }
-  const int e = (int)(__float_as_uint(s) >> 23) - 127;                // -6 .. 8
-  const float t = s * __uint_as_float((uint32_t)(130 - e) << 23);    // s * 2^(3-e) in [8,16)
-  const uint32_t m = (uint32_t)__builtin_rintf(t);                   // 8 .. 16
-  return ((uint32_t)(e + 7) << 3) + (m - 8u);
+// Largest |t_i| of t = H16 * diag(d) * x as binary32 bits, without forming the last
+// stage: for its pair (a, b), max(|a + b|, |a - b|) = |a| + |b| exactly, and rounding to
+// nearest is monotonic and sign-symmetric, so the larger of the two rounded magnitudes is
+// the rounded |a| + |b|.  Non-finite inputs give a result >= 0x7F800000.
+__device__ __forceinline__ uint32_t rht16_absmax_bits(float v[16], uint32_t signmask) {
+  rht16_signs(v, signmask);
+  rht16_stage(v, 1);
+  rht16_stage(v, 2);
+  rht16_stage(v, 4);
+  uint32_t m = 0u;   // integer max of the bit patterns: a NaN is kept, not dropped
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    m = max(m, __float_as_uint(fabsf(v[i]) + fabsf(v[i + 8])) & 0x7FFFFFFFu);
+  return m;
 }
 
-// Value of an E4M3FN code 0..0x7E (block scales are never negative or NaN).
+// ---------------------------------------------------------------- E4M3
+// Nearest-even E4M3FN code of s >= 0, saturating to 448 (code 0x7E).  The hardware
+// conversion rounds to nearest-even over the normal and subnormal E4M3 grid; clamping at
+// 448 first gives the saturation (values from 464 up would otherwise become NaN).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, kE4M3Max), 0.0f, 0, false) & 0xFFu;
+}
+
+// Value of an E4M3FN code (exact).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e == 0 ? (float)m * 0.001953125f
-                : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+
+// a / 6 rounded to nearest-even.  q0 = a * RN(1/6) is within an ulp; the residual
+// a - 6 q0 is exact under FMA, and one correction step q0 + residual * RN(1/6) lands on
+// the correctly rounded quotient for every binary32 a >= 2^-125 (an exhaustive property
+// of binary32; the CPU tests check it).  Smaller a, where the residual is no longer
+// exact, take the division.
+__device__ __forceinline__ float div6(float a) {
+  if (__float_as_uint(a) < 0x01000000u) return a / 6.0f;
+  const float c = 1.0f / 6.0f;
+  const float q0 = a * c;
+  const float r = __builtin_fmaf(-q0, 6.0f, a);
+  return __builtin_fmaf(r, c, q0);
 }
 
 // ---------------------------------------------------------------- E2M1

@@ -7,22 +7,235 @@
 // scale from the tensor amax, an E4M3 scale per 1x16 or 16x16 block, E2M1 codes by
 // nearest-even or stochastic rounding (Philox4x32-10 keyed on (seed, element index)).
 //
-// The tensor scale needs the amax of the whole (transformed) tensor before any code can
-// be written, so quantization is two passes over the input:
-//   pass 1  amax_kernel: each workgroup reduces a contiguous range of row groups to one
-//           partial amax (integer max of |y| bit patterns: exact and order-free);
-//   pass 2  quant_1x16_kernel / quant_16x16_kernel: every workgroup reduces the partials,
-//           derives the tensor scales on the device (no host sync), and encodes its range.
-// Pass 2 re-reads an input that pass 1 has just streamed, which the 256 MB Infinity
-// Cache holds for the sizes this library targets.
+// No code can be written before the amax of the whole (transformed) tensor is known.  One
+// kernel per blocking reads the input once when the tensor fits in the registers of the
+// resident workgroups:
+//   phase 1  workgroup b owns chunks b, b + grid, b + 2 grid, ...; it loads each into
+//            registers and publishes the chunk's partial amax (integer max of |y| bit
+//            patterns: exact and order-free) as one 64-bit word, (launch tag << 32) | amax,
+//            in the caller's workspace;
+//   collect  workgroup 0 reads every chunk's word and publishes the tensor amax the same
+//            way; the others poll that one word;
+//   phase 2  every workgroup encodes the chunk still held in its registers, then re-reads
+//            and encodes any other chunk it owns.
+// Words written by an earlier launch carry another tag, so the words are never cleared;
+// the only shared read-modify-write is one arrival count per workgroup, off the critical
+// path (an atomic or a fence on a shared address costs about 10 ns per workgroup on this
+// chip, serialised).  A workgroup never needs another
+// to be resident: one that has waited 100 us computes the missing partial maxima itself
+// (publishing a word twice writes the same value), so every wait ends.
+#include <stdlib.h>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// ---------------------------------------------------------------- coordination
+// Workspace: the header, then one uint64_t word per chunk at kCoordBytes.  The tag of a
+// launch is epoch + 1, read by every workgroup when it starts.  After its phase 1 each
+// workgroup counts itself: workgroup b in counter b % 32 (each on its own 128-byte line,
+// so that no more than a few dozen atomics queue on one address), the last of a group in
+// `top`, and the last of all sets epoch to this launch's tag; every workgroup has read the
+// epoch by then.  So every launch, a replay of a captured graph included, gets a tag that
+// no word of the previous launch has.  The workspace must be zero-filled before its first
+// use; the counters return to zero at the end of every launch.
+constexpr uint32_t kArriveGroups = 32;
+struct Header {
+  uint64_t gword;    // tensor amax of the current launch, tagged
+  uint32_t epoch;    // tag of the last launch whose workgroups all arrived
+  uint32_t top;      // groups of the current launch whose workgroups all arrived
+  uint32_t pad[28];
+  struct alignas(128) Line { uint32_t n; } sub[kArriveGroups];   // arrivals per group
+};
+static_assert(sizeof(Header) <= kCoordBytes, "workspace header");
+template <typename U>
+__device__ __forceinline__ U load_relaxed(const U *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename U>
+__device__ __forceinline__ void store_relaxed(U *p, U v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t tok, uint32_t v) {
+  return ((uint64_t)tok << 32) | (uint64_t)v;
+}
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tok) {
+  return (uint32_t)(w >> 32) == tok;
+}
+
+// This launch's tag (the same in every workgroup of the launch).
+__device__ __forceinline__ uint32_t wg_tag(Header *h, uint32_t *slot) {
+  if (threadIdx.x == 0) slot[0] = load_relaxed(&h->epoch);
+  __syncthreads();
+  uint32_t tok = slot[0] + 1u;
+  __syncthreads();
+  return tok == 0u ? 1u : tok;
+}
+
+// A wait this long (ticks of the 100 MHz constant clock) means some owner is not running:
+// the waiter then computes what is missing itself.  The environment variable
+// NVFP4_HELP_DELAY_TICKS overrides it (0 makes every waiter help at once, which tests use
+// to exercise that path).
+constexpr uint64_t kHelpTicks = 10000ull;       // 100 us
+// Last-resort limit of a wait (5 s): turns a broken argument above into an error status.
+constexpr uint64_t kFailTicks = 500000000ull;
+
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+
+template <int I>
+struct Idx { static constexpr int value = I; };
+
+// f(Idx<0>{}), ..., f(Idx<N-1>{}): every index is a compile-time constant, so a chunk held
+// in register arrays is never indexed dynamically (which would move it to scratch memory).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(Idx<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ uint32_t wg_max(uint32_t m, uint32_t *red) {
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < T / 64; ++i) r = max(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int T>
+__device__ __forceinline__ uint32_t wg_min(uint32_t m, uint32_t *red) {
+  m = ~wg_max<T>(~m, red);
+  return m;
+}
+
+// Count this workgroup's arrival; the last arrival of the launch publishes the launch's
+// tag as the new epoch.  The first lane of the last wave does it, so that the waits for
+// these atomics delay no wave that collects the tensor amax.
+template <int T>
+__device__ __forceinline__ void wg_arrive(Header *h, uint32_t tok) {
+  if (threadIdx.x != T - 64) return;
+  const uint32_t ng = gridDim.x < kArriveGroups ? gridDim.x : kArriveGroups;
+  const uint32_t j = blockIdx.x % ng;
+  const uint32_t members = (gridDim.x - j + ng - 1) / ng;   // workgroups b with b % ng == j
+  uint32_t *sub = &h->sub[j].n;
+  if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != members - 1)
+    return;
+  store_relaxed(sub, 0u);
+  if (__hip_atomic_fetch_add(&h->top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ng - 1)
+    return;
+  store_relaxed(&h->top, 0u);
+  store_relaxed(&h->epoch, tok);
+}
+
+// Collect the tensor amax from the chunk words.  partial(c) computes chunk c's partial
+// maximum with the whole workgroup (used only for chunks still missing after the help
+// delay).  Each thread follows its own words c = tid + k*T; the returned value is the
+// same in every thread.
+template <int T, typename Partial>
+__device__ __forceinline__ uint32_t wg_collect(uint64_t *words, uint32_t nchunks, uint32_t tok,
+                                               uint64_t help, uint32_t *red, uint32_t *slot,
+                                               bool *failed, Partial &&partial) {
+  uint32_t m = 0;
+  uint32_t next = threadIdx.x;                 // first word not yet seen ready
+  const uint64_t t0 = (uint64_t)wall_clock64();   // thread 0's reading decides for all
+  *failed = false;
+  for (;;) {
+    // read ahead: up to 8 words in flight per thread
+    while (next < nchunks) {
+      uint64_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t c = next + (uint32_t)k * T;
+        w[k] = c < nchunks ? load_relaxed(words + c) : tagged(tok, 0u);
+      }
+      int ready = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (ready == k && has_tag(w[k], tok)) {
+          m = max(m, (uint32_t)w[k]);
+          ++ready;
+        }
+      }
+      next += (uint32_t)ready * T;
+      if (ready < 8) break;
+    }
+    const uint32_t pending = wg_min<T>(next < nchunks ? next : kNone, red);
+    if (pending == kNone) break;
+    // one decision for the whole workgroup: 0 wait, 1 help, 2 give up
+    if (threadIdx.x == 0) {
+      const uint64_t waited = (uint64_t)wall_clock64() - t0;
+      slot[0] = waited > kFailTicks ? 2u : (waited >= help ? 1u : 0u);
+    }
+    __syncthreads();
+    const uint32_t decision = slot[0];
+    __syncthreads();
+    if (decision == 2u) {
+      *failed = true;
+      break;
+    }
+    if (decision == 1u) {
+      const uint32_t pm = partial(pending);          // whole workgroup
+      if (threadIdx.x == 0) store_relaxed(words + pending, tagged(tok, pm));
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  return wg_max<T>(m, red);
+}
+
+// The tensor amax.  When every workgroup can afford to read all chunk words (at most
+// 64K words over the grid per polling round) each collects it directly; otherwise
+// workgroup 0 collects and publishes it in the global word, which the others poll, and
+// a workgroup that has waited past the help delay collects it itself.
+template <int T, typename Partial>
+__device__ __forceinline__ uint32_t wg_amax(uint64_t *gword, uint64_t *words, uint32_t nchunks,
+                                            uint32_t tok, uint64_t help, uint32_t *red,
+                                            uint32_t *slot, bool *failed, Partial &&partial) {
+  if ((uint64_t)gridDim.x * nchunks <= 65536u)
+    return wg_collect<T>(words, nchunks, tok, help, red, slot, failed, partial);
+  if (blockIdx.x == 0) {
+    const uint32_t m = wg_collect<T>(words, nchunks, tok, help, red, slot, failed, partial);
+    if (threadIdx.x == 0 && !*failed) store_relaxed(gword, tagged(tok, m));
+    return m;
+  }
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = (uint64_t)wall_clock64();
+    uint64_t g = load_relaxed(gword);
+    while (!has_tag(g, tok) && (uint64_t)wall_clock64() - t0 < help) {
+      __builtin_amdgcn_s_sleep(16);
+      g = load_relaxed(gword);
+    }
+    slot[0] = has_tag(g, tok) ? 1u : 0u;
+    slot[1] = (uint32_t)g;
+  }
+  __syncthreads();
+  const bool ready = slot[0] != 0;
+  const uint32_t gm = slot[1];
+  __syncthreads();
+  if (ready) {
+    *failed = false;
+    return gm;
+  }
+  return wg_collect<T>(words, nchunks, tok, help, red, slot, failed, partial);
+}
+
+// Workgroup 0 publishes the tensor scale and the status: 0, 1 for a non-finite input,
+// 2 if a wait passed the last-resort limit.
+__device__ __forceinline__ void wg_publish_scale(bool failed, const TensorScale &ts,
+                                                 float *global_dec, uint32_t *dev_status) {
+  if (threadIdx.x == 0 && (blockIdx.x == 0 || failed)) {
+    *global_dec = failed ? __uint_as_float(0x7FC00000u) : ts.dec;
+    if (dev_status) *dev_status = failed ? 2u : (ts.finite ? 0u : 1u);
+  }
+}
 
 __device__ __forceinline__ uint32_t rht_signmask(uint32_t k0, uint32_t k1) {
   // Sign vector: bit j of word 0 of Philox4x32-10(key = seed, counter = (0, 0, 1, 0)).
@@ -37,74 +250,30 @@ __device__ __forceinline__ const uint4 *group_ptr(const uint16_t *x, uint32_t g,
   return reinterpret_cast<const uint4 *>(x + (size_t)r * (size_t)ld + (size_t)gc * 16u);
 }
 
-__device__ __forceinline__ uint32_t block_max_bits(uint32_t m) {
-  __shared__ uint32_t red[kWaves];
-  m = wave_max_u32(m);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = m;
-  __syncthreads();
-  uint32_t r = red[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = max(r, red[i]);
-  __syncthreads();
-  return r;
-}
-
-// ---------------------------------------------------------------- pass 1
-template <bool RHT, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restrict__ x,
-                                                        uint32_t ngroups, uint32_t gpr,
-                                                        int64_t ld, uint32_t rk0,
-                                                        uint32_t rk1, uint32_t per_wg,
-                                                        uint32_t *__restrict__ partials) {
-  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
-  const uint32_t begin = blockIdx.x * per_wg;
-  const uint32_t end = min(begin + per_wg, ngroups);
-  uint32_t m = 0;
-  constexpr int U = 4;   // row groups in flight per thread
-  for (uint32_t g0 = begin + threadIdx.x; g0 < end; g0 += U * kThreads) {
-    uint4 a[U], b[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t g = g0 + u * kThreads;
-      if (g < end) {
-        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
-        a[u] = p[0];
-        b[u] = p[1];
-      } else {
-        a[u] = make_uint4(0u, 0u, 0u, 0u);
-        b[u] = a[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v[16];
-      unpack16(a[u], b[u], v);
-      if (RHT) rht16(v, sm);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
-    }
+// Block multipliers for the 127 codes a block scale can take, built once per workgroup:
+// rtab[c] = s_enc / decode(c), 0 for the zero scale.  With quarter set (RHT input), the
+// transform's final 1/4 moves into the table, t * (r / 4) in place of (t / 4) * r, when
+// that is exact for every element; the function returns whether it did.  Both forms round
+// the same real product when t / 4 and r / 4 are exact (r >= 2^-124).  Where t / 4 is not
+// (|t| < 2^-124) and r < 2^108, both products stay below 2^-18 in magnitude with the sign
+// of t: a zero code under nearest rounding, and never a step up under stochastic
+// rounding, whose smallest threshold is 2^-17 of a step.
+__device__ __forceinline__ bool build_rtab(float *rtab, float s_enc, bool quarter) {
+  const uint32_t c = threadIdx.x;
+  float r = 0.0f;
+  bool ok = true;
+  if (c < 128u) {
+    r = c == 127u ? 0.0f : block_mult(s_enc, e4m3_decode(c));   // 127 is NaN, never made
+    ok = r == 0.0f || (r >= 0x1p-124f && r < 0x1p108f);
   }
-  m = block_max_bits(m);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  const bool all_ok = __syncthreads_and(ok) != 0;
+  const bool fold = quarter && all_ok;
+  if (c < 128u) rtab[c] = fold ? 0.25f * r : r;
+  __syncthreads();
+  return fold;
 }
 
-// Reduce the partial maxima of pass 1 and publish the tensor scale (workgroup 0).
-__device__ __forceinline__ TensorScale finish_amax(const uint32_t *__restrict__ partials,
-                                                   uint32_t nparts, float *global_dec,
-                                                   uint32_t *dev_status) {
-  uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partials[i]);
-  m = block_max_bits(m);
-  const TensorScale ts = tensor_scale(m);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    *global_dec = ts.dec;
-    if (dev_status) *dev_status = ts.finite ? 0u : 1u;
-  }
-  return ts;
-}
-
-// Encode the 16 transformed values of one row group with the block multiplier rr.
+// Encode the 16 values of one row group times the block multiplier rr.
 // k[16]: 16-bit random integers (stochastic rounding only).
 template <bool SR>
 __device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uint32_t k[16]) {
@@ -113,7 +282,7 @@ __device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uin
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float a = fabsf(y[j] * rr);
-    const uint32_t mag = SR ? e2m1_sr_mag(a, k[j]) : e2m1_rn_mag(a);
+    const uint32_t mag = e2m1_sr_mag(a, k[j]);
     const uint32_t q = mag | ((__float_as_uint(y[j]) >> 28) & 8u);
     if (j < 8) lo |= q << (4 * j);
     else hi |= q << (4 * (j - 8));
@@ -142,15 +311,223 @@ __device__ __forceinline__ float absmax16(const float v[16]) {
   return m;
 }
 
-// ---------------------------------------------------------------- pass 2, 1x16
-// One row group per thread per step; the next step's 32 input bytes are loaded before
+__device__ __forceinline__ uint4 mask4(const uint4 &v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// ---------------------------------------------------------------- 1x16
+// A chunk is kG1 * kT1 consecutive row groups; thread t holds groups base + i*kT1 + t,
+// i < kG1, so every load and store instruction of a wave covers consecutive memory.
+constexpr int kT1 = 512;
+constexpr int kG1 = 20;
+constexpr uint32_t kChunk1 = (uint32_t)kT1 * kG1;
+
+// Two waves per SIMD (one workgroup per CU): up to 256 registers per lane for the chunk.
+// Nearest-even rounding only.
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) void quant_1x16_kernel(
+    const uint16_t *__restrict__ x, uint32_t ngroups, uint32_t gpr, int64_t ld, int64_t cols,
+    uint32_t rk0, uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base,
+    uint32_t nchunks, uint64_t help, void *__restrict__ ws, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ global_dec,
+    uint32_t *dev_status) {
+  __shared__ float rtab[128];
+  __shared__ uint32_t red[kT1 / 64];
+  __shared__ uint32_t slot[2];
+  Header *hdr = static_cast<Header *>(ws);
+  uint64_t *gword = &hdr->gword;
+  uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
+  const uint32_t tok = wg_tag(hdr, slot);
+  const uint32_t tid = threadIdx.x;
+  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
+  constexpr bool SR = false;   // stochastic rounding takes the two-pass kernels below
+  uint4 ra[kG1], rb[kG1];
+
+  auto load_chunk = [&](uint32_t c) __attribute__((always_inline)) {
+    const uint32_t base = c * kChunk1;
+    static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      const uint32_t g = base + (uint32_t)i * kT1 + tid;
+      const bool valid = g < ngroups;
+      const uint4 *p = group_ptr<CONTIG>(x, valid ? g : base, gpr, ld);
+      const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
+      ra[i] = mask4(p[0], m);
+      rb[i] = mask4(p[1], m);
+    });
+  };
+  auto group_max = [&](const uint4 &a, const uint4 &b) __attribute__((always_inline)) {
+    float v[16];
+    unpack16(a, b, v);
+    if (RHT) return rht16_absmax_bits(v, sm);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+    return m;
+  };
+  // partial maximum of chunk c streamed from memory (for a chunk whose owner is late)
+  auto partial = [&](uint32_t c) __attribute__((always_inline)) {
+    const uint32_t base = c * kChunk1;
+    uint32_t m = 0;
+    for (int i = 0; i < kG1; ++i) {
+      const uint32_t g = base + (uint32_t)i * kT1 + tid;
+      if (g < ngroups) {
+        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+        m = max(m, group_max(p[0], p[1]));
+      }
+    }
+    return wg_max<kT1>(m, red);
+  };
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold) __attribute__((always_inline)) {
+    const uint32_t base = c * kChunk1;
+    static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      const uint32_t g = base + (uint32_t)i * kT1 + tid;
+      if (g < ngroups) {
+        float v[16];
+        unpack16(ra[i], rb[i], v);
+        if (RHT) rht16_unscaled(v, sm);           // v = 4 y
+        const float bmax = RHT ? absmax16(v) * 0.25f : absmax16(v);
+        const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
+        const float rr = rtab[sb];
+        if (RHT && !fold) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+        }
+        uint32_t k[16];
+        if (SR) {
+          const uint32_t r = g / gpr, gc = g - r * gpr;
+          sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, k);
+        }
+        reinterpret_cast<uint2 *>(codes)[g] = encode16<SR>(v, rr, k);  // group g at byte 8g
+        scales[g] = (uint8_t)sb;
+      }
+    });
+  };
+
+  // phase 1: the chunks this workgroup owns; the last one stays in registers
+  uint32_t last = kNone;
+  for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    load_chunk(c);
+    uint32_t m = 0;
+    static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      m = max(m, group_max(ra[i], rb[i]));
+    });
+    m = wg_max<kT1>(m, red);
+    if (tid == 0) store_relaxed(words + c, tagged(tok, m));
+    last = c;
+  }
+
+  wg_arrive<kT1>(hdr, tok);
+
+  // tensor scale
+  bool failed;
+  uint32_t am = wg_amax<kT1>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
+  const TensorScale ts = tensor_scale(am);
+  wg_publish_scale(failed, ts, global_dec, dev_status);
+
+  // phase 2
+  if (ts.finite && !failed) {
+    const bool fold = build_rtab(rtab, ts.enc, RHT);
+    if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
+      encode_chunk(last, ts, fold);
+      for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
+        load_chunk(c);
+        encode_chunk(c, ts, fold);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 1x16, stochastic
+// Stochastic rounding spends most of its time in the Philox draws, whose dependent
+// multiply chains need many resident waves to hide their latency; the register-resident
+// kernel above runs two waves per SIMD.  This path reads the input twice instead:
+//   pass 1  amax_kernel: each workgroup reduces a contiguous range of row groups to one
+//           partial amax in the workspace;
+//   pass 2  quant_1x16_sr_kernel: every workgroup reduces the partials and encodes its
+//           range, eight resident workgroups per CU.
+constexpr int kThreads = 256;
+constexpr uint32_t kAmaxMaxWg = 1024;   // pass-1 workgroups (each writes one partial)
+constexpr uint32_t kSrMaxWg = 2048;     // pass-2 workgroups: eight per CU
+
+// pass 1
+
+// Partial maxima of |t| as bit patterns, where t is the row group itself or, with the
+// RHT, H16 * diag(d) * x before the final quarter (applied once to the tensor maximum:
+// rounding is monotonic, so max |RN(t / 4)| = RN(max |t| / 4)).
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restrict__ x,
+                                                        uint32_t ngroups, uint32_t gpr,
+                                                        int64_t ld, uint32_t rk0,
+                                                        uint32_t rk1, uint32_t per_wg,
+                                                        uint32_t *__restrict__ partials) {
+  __shared__ uint32_t red[kThreads / 64];
+  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
+  const uint32_t begin = blockIdx.x * per_wg;
+  const uint32_t end = min(begin + per_wg, ngroups);
+  uint32_t m = 0;
+  constexpr int U = 4;   // row groups in flight per thread
+  for (uint32_t g0 = begin + threadIdx.x; g0 < end; g0 += U * kThreads) {
+    uint4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t g = g0 + u * kThreads;
+      if (g < end) {
+        const uint4 *p = group_ptr<CONTIG>(x, g, gpr, ld);
+        a[u] = p[0];
+        b[u] = p[1];
+      } else {
+        a[u] = make_uint4(0u, 0u, 0u, 0u);
+        b[u] = a[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[16];
+      unpack16(a[u], b[u], v);
+      if (RHT) {
+        m = max(m, rht16_absmax_bits(v, sm));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+      }
+    }
+  }
+  m = wg_max<kThreads>(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Reduce the partial maxima of pass 1 and publish the tensor scale (workgroup 0).
+template <bool RHT>
+__device__ __forceinline__ TensorScale finish_amax(const uint32_t *__restrict__ partials,
+                                                   uint32_t nparts, float *global_dec,
+                                                   uint32_t *dev_status, uint32_t *red) {
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partials[i]);
+  m = wg_max<kThreads>(m, red);
+  if (RHT && m < 0x7F800000u) m = __float_as_uint(__uint_as_float(m) * 0.25f);
+  const TensorScale ts = tensor_scale(m);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *global_dec = ts.dec;
+    if (dev_status) *dev_status = ts.finite ? 0u : 1u;
+  }
+  return ts;
+}
+
+// pass 2: one row group per thread per step; the next step's 32 input bytes are loaded before
 // the current group is encoded, so every wave keeps a load in flight while it computes.
-template <bool RHT, bool SR, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
+// Block scale: sb = e4m3((amax_b / 6) * s_enc); codes: e2m1(y * r) with r = s_enc / sb
+// from the workgroup's table.
+template <bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
     const uint16_t *__restrict__ x, uint32_t ngroups, uint32_t gpr, int64_t ld, int64_t cols,
     uint32_t rk0, uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base, uint32_t per_wg,
     const uint32_t *__restrict__ partials, uint32_t nparts, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_dec, uint32_t *dev_status) {
+  constexpr bool SR = true;
+  __shared__ float rtab[128];
+  __shared__ uint32_t red[kThreads / 64];
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
   uint32_t g = begin + threadIdx.x;
@@ -162,8 +539,9 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
     ca = p[0];
     cb = p[1];
   }
-  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
+  const TensorScale ts = finish_amax<RHT>(partials, nparts, global_dec, dev_status, red);
   if (!ts.finite) return;
+  const bool fold = build_rtab(rtab, ts.enc, RHT);
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   for (; g < end; g += kThreads) {
     // next group (on the last step this re-reads the current one: always a valid address)
@@ -172,10 +550,14 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
     const uint4 na = pn[0], nb = pn[1];
     float v[16];
     unpack16(ca, cb, v);
-    if (RHT) rht16(v, sm);
-    const float bmax = absmax16(v);
-    const uint32_t sb = e4m3_encode((bmax / kE2M1Max) * ts.enc);
-    const float rr = block_mult(ts.enc, e4m3_decode(sb));
+    if (RHT) rht16_unscaled(v, sm);           // v = 4 y
+    const float bmax = RHT ? absmax16(v) * 0.25f : absmax16(v);
+    const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
+    const float rr = rtab[sb];
+    if (RHT && !fold) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+    }
     uint32_t k[16];
     if (SR) {
       const uint32_t r = g / gpr, gc = g - r * gpr;
@@ -188,159 +570,256 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_kernel(
   }
 }
 
-// ---------------------------------------------------------------- pass 2, 16x16
-// A workgroup encodes a block of 16 x 16 tiles (256 x 256 elements) in 16 steps, one
-// tile-row of 16 tiles per step; 16 lanes of a DPP row hold the 16 rows of a tile.  The
-// tile amax is a DPP max over the row.  Codes of x are stored per step (128 contiguous
-// bytes per row); with TRANS the codes of x^T come from an in-register 4-bit transpose and
-// are assembled in LDS so that each of the block's 256 rows of x^T is written as one
-// 128-byte line at the end (a row of x^T receives 8 bytes per tile-row of x).
-constexpr int kTStride = 136;   // LDS bytes per staged x^T row (128 + 8 against bank conflicts)
+// ---------------------------------------------------------------- 16x16
+// A chunk is a block of up to kG16 tile-rows x 16 tile columns (128 x 256 elements); the
+// 16 lanes of a DPP row hold the 16 rows of a tile, one tile-row per step, and the tile
+// amax is a DPP max over the row.  Codes of x are stored per step; with TRANS the codes
+// of x^T come from an in-register 4-bit transpose and are assembled in LDS, so that each
+// of the chunk's 256 rows of x^T is written as one segment of 8 bytes per tile-row.
+constexpr int kT16 = 256;
+constexpr int kG16 = 8;
+constexpr int kTStride = kG16 * 8 + 8;   // LDS bytes per staged x^T row (+8 against bank conflicts)
 
 template <bool SR, bool TRANS>
-__global__ __launch_bounds__(kThreads) void quant_16x16_kernel(
+__global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sk0,
-    uint32_t sk1, uint64_t sr_base, const uint32_t *__restrict__ partials, uint32_t nparts,
+    uint32_t sk1, uint64_t sr_base, uint32_t nchunks, uint64_t help, void *__restrict__ ws,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
     uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTStride : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 256 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 16 * kG16 : 16];
+  __shared__ float rtab[128];
+  __shared__ uint32_t red[kT16 / 64];
+  __shared__ uint32_t slot[2];
+  Header *hdr = static_cast<Header *>(ws);
+  uint64_t *gword = &hdr->gword;
+  uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
+  const uint32_t tok = wg_tag(hdr, slot);
   const uint32_t tpr = (uint32_t)(cols >> 4);          // tiles per tile-row
   const uint32_t tpc = (uint32_t)(rows >> 4);          // tiles per tile-column
-  if (tpr == 0 || tpc == 0) {   // empty tensor: only the tensor scale is written
-    finish_amax(partials, nparts, global_dec, dev_status);
-    return;
-  }
-  const uint32_t bpr = (tpr + 15) >> 4;                // blocks per block-row
-  const uint32_t blk = blockIdx.x;
-  const uint32_t br = blk / bpr, bc = blk - br * bpr;
+  const uint32_t cpr = (tpr + 15) >> 4;                // chunks per chunk-row
   const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
-  const uint32_t tc = bc * 16 + tl;                    // this lane's tile column
-  const bool col_ok = tc < tpr;
-  // every lane loads a valid address (the block's first tile when past an edge) and
-  // masks the data, so the 16 lanes of a tile always run the reductions together
-  auto load = [&](uint32_t it, uint4 &a, uint4 &b) {
-    const uint32_t tr = br * 16 + it;
-    const bool valid = col_ok && tr < tpc;
-    const uint32_t rr_ = valid ? tr : br * 16, cc = valid ? tc : bc * 16;
-    const uint4 *p = reinterpret_cast<const uint4 *>(x + ((int64_t)rr_ * 16 + r) * ld + (int64_t)cc * 16);
-    const uint4 ra = p[0], rb = p[1];
-    const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
-    a = make_uint4(ra.x & m, ra.y & m, ra.z & m, ra.w & m);
-    b = make_uint4(rb.x & m, rb.y & m, rb.z & m, rb.w & m);
+  uint4 ra[kG16], rb[kG16];
+
+  auto load_chunk = [&](uint32_t c) __attribute__((always_inline)) {
+    const uint32_t br = c / cpr, bc = c - br * cpr;
+    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tc = bc * 16 + tl;
+    const bool col_ok = tc < tpr;
+    // a lane past the right edge loads the chunk's first tile (a valid address) and masks
+    // the data, so the 16 lanes of a tile always run the reductions together
+    const uint16_t *lane = x + ((int64_t)tr0 * 16 + r) * ld + (int64_t)(col_ok ? tc : bc * 16) * 16;
+    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+      constexpr int it = decltype(I)::value;
+      const bool valid = col_ok && (uint32_t)it < nit;
+      const uint4 *p = reinterpret_cast<const uint4 *>(lane + (int64_t)((uint32_t)it < nit ? it : 0) * 16 * ld);
+      const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
+      ra[it] = mask4(p[0], m);
+      rb[it] = mask4(p[1], m);
+    });
   };
-  uint4 ca, cb;
-  load(0, ca, cb);                    // in flight while the tensor scale is reduced
-  const TensorScale ts = finish_amax(partials, nparts, global_dec, dev_status);
-  if (!ts.finite) return;
-  const uint32_t nit = min(16u, tpc - br * 16);
-  for (uint32_t it = 0; it < nit; ++it) {
-    uint4 na, nb;
-    load(it + 1 < nit ? it + 1 : it, na, nb);
-    const uint32_t tr = br * 16 + it;
-    const int64_t row = (int64_t)tr * 16 + r;
-    float v[16];
-    unpack16(ca, cb, v);
-    const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
-    const uint32_t sb = e4m3_encode((__uint_as_float(tmax) / kE2M1Max) * ts.enc);
-    const float rr = block_mult(ts.enc, e4m3_decode(sb));
-    uint32_t k[16];
-    if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
-    uint2 q = encode16<SR>(v, rr, k);
-    if (col_ok) {
-      *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
-      if (r == 0) scales[(size_t)tr * tpr + tc] = (uint8_t)sb;
-    }
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts) __attribute__((always_inline)) {
+    const uint32_t br = c / cpr, bc = c - br * cpr;
+    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tc = bc * 16 + tl;
+    const bool col_ok = tc < tpr;
+    if (TRANS) __syncthreads();   // the previous chunk's write-out has read the stage
+    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+      constexpr int it = decltype(I)::value;
+      if ((uint32_t)it < nit) {   // uniform over the workgroup
+        const uint32_t trw = tr0 + it;
+        const int64_t row = (int64_t)trw * 16 + r;
+        float v[16];
+        unpack16(ra[it], rb[it], v);
+        const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
+        const uint32_t sb = e4m3_encode(div6(__uint_as_float(tmax)) * ts.enc);
+        const float rr = rtab[sb];
+        uint32_t k[16];
+        if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
+        uint2 q = encode16<SR>(v, rr, k);
+        if (col_ok) {
+          *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
+          if (r == 0) scales[(size_t)trw * tpr + tc] = (uint8_t)sb;
+        }
+        if (TRANS) {
+          transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
+          *reinterpret_cast<uint2 *>(tbuf + (tl * 16 + r) * kTStride + it * 8) = q;
+          if (r == 0) sbuf[tl * kG16 + it] = (uint8_t)sb;
+        }
+      }
+    });
     if (TRANS) {
-      transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
-      *reinterpret_cast<uint2 *>(tbuf + (tl * 16 + r) * kTStride + it * 8) = q;
-      if (r == 0) sbuf[tl * 16 + it] = (uint8_t)sb;
-    }
-    ca = na;
-    cb = nb;
-  }
-  if (TRANS) {
-    __syncthreads();
-    // 256 staged rows of x^T, nit * 8 bytes each: row j of the block is x^T row
-    // bc*256 + j, bytes [br*128, br*128 + 8*nit)
-    const uint32_t nbytes = nit * 8;
-    for (uint32_t i = threadIdx.x; i < 256 * 16; i += kThreads) {
-      const uint32_t j = i >> 4, c8 = i & 15u;     // row, 8-byte chunk
-      const uint32_t ttc = bc * 16 + (j >> 4);
-      if (ttc < tpr && c8 * 8 < nbytes) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTStride + c8 * 8);
-        const int64_t trow = (int64_t)bc * 256 + j;
-        *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)br * 128 + c8 * 8) = w;
+      __syncthreads();
+      // 256 staged rows of x^T, nit * 8 bytes each: row j of the chunk is x^T row
+      // bc*256 + j, bytes [tr0*8, tr0*8 + 8*nit)
+      for (uint32_t i = threadIdx.x; i < 256u * kG16; i += kT16) {
+        const uint32_t j = i / kG16, c8 = i % kG16;   // row, 8-byte piece
+        const uint32_t ttc = bc * 16 + (j >> 4);
+        if (ttc < tpr && c8 < nit) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTStride + c8 * 8);
+          const int64_t trow = (int64_t)bc * 256 + j;
+          *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr0 * 8 + c8 * 8) = w;
+        }
+      }
+      // scales of x^T: row ttc (one per tile column), bytes [tr0, tr0 + nit)
+      if (threadIdx.x < 16u * kG16) {
+        const uint32_t tcl = threadIdx.x / kG16, it = threadIdx.x % kG16;
+        const uint32_t ttc = bc * 16 + tcl;
+        if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + tr0 + it] = sbuf[tcl * kG16 + it];
       }
     }
-    // scales of x^T: row tc (one per tile column), bytes [br*16, br*16 + nit)
-    if (threadIdx.x < 256) {
-      const uint32_t tcl = threadIdx.x >> 4, it = threadIdx.x & 15u;
-      const uint32_t ttc = bc * 16 + tcl;
-      if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + br * 16 + it] = sbuf[tcl * 16 + it];
+  };
+
+  auto lane_max = [&](const uint4 &a, const uint4 &b) __attribute__((always_inline)) {
+    float v[16];
+    unpack16(a, b, v);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+    return m;
+  };
+  // partial maximum of chunk c streamed from memory (for a chunk whose owner is late)
+  auto partial = [&](uint32_t c) __attribute__((always_inline)) {
+    const uint32_t br = c / cpr, bc = c - br * cpr;
+    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tc = bc * 16 + tl;
+    uint32_t m = 0;
+    if (tc < tpr) {
+      const uint16_t *lane = x + ((int64_t)tr0 * 16 + r) * ld + (int64_t)tc * 16;
+      for (uint32_t it = 0; it < nit; ++it) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(lane + (int64_t)it * 16 * ld);
+        m = max(m, lane_max(p[0], p[1]));
+      }
+    }
+    return wg_max<kT16>(m, red);
+  };
+
+  // phase 1: the chunks this workgroup owns; the last one stays in registers
+  uint32_t last = kNone;
+  for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    load_chunk(c);
+    uint32_t m = 0;
+    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+      constexpr int it = decltype(I)::value;
+      m = max(m, lane_max(ra[it], rb[it]));
+    });
+    m = wg_max<kT16>(m, red);
+    if (threadIdx.x == 0) store_relaxed(words + c, tagged(tok, m));
+    last = c;
+  }
+
+  wg_arrive<kT16>(hdr, tok);
+
+  bool failed;
+  const uint32_t am = wg_amax<kT16>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  const TensorScale ts = tensor_scale(am);
+  wg_publish_scale(failed, ts, global_dec, dev_status);
+
+  if (ts.finite && !failed) {
+    build_rtab(rtab, ts.enc, false);
+    if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
+      encode_chunk(last, ts);
+      for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
+        load_chunk(c);
+        encode_chunk(c, ts);
+      }
     }
   }
 }
 
-uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
-// Workgroup caps of the encode pass (8 resident 256-thread workgroups per CU).
-#ifndef NVFP4_Q1_MAX_WG
-#define NVFP4_Q1_MAX_WG 2048
-#endif
-#ifndef NVFP4_AMAX_MAX_WG
-#define NVFP4_AMAX_MAX_WG 1024
-#endif
+// Resident workgroups per CU of a kernel, times the CU count: the grid that gives every
+// resident slot one chunk.  A smaller number of resident workgroups is still correct.
+// Cached per device and kernel (the race on the cache is benign: every writer stores the
+// same value).
+template <typename K>
+uint32_t resident_grid(K kernel, int threads) {
+  static uint32_t cache[64] = {};
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
+                                                   threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const uint32_t g = (uint32_t)(cus * per_cu);
+  if (dev >= 0 && dev < 64) cache[dev] = g;
+  return g;
+}
 
 }  // namespace
 
+uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding) {
+  if (blocking == 0) {
+    if (rounding == 1) return (kAmaxMaxWg * 4 + 7) / 8;   // pass-1 partials
+    return ceil_div((uint64_t)rows * (uint64_t)(cols / 16), kChunk1);
+  }
+  return ceil_div((uint64_t)(rows / 16), kG16) * ceil_div((uint64_t)(cols / 16), 16);
+}
+
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
-  const uint64_t ngroups64 = (uint64_t)q.rows * (uint64_t)(q.cols / 16);
-  const uint32_t ngroups = (uint32_t)ngroups64;
-  const uint32_t gpr = (uint32_t)(q.cols / 16);
-  const bool contig = (q.ld == q.cols);
-  // pass 1 geometry: up to 1024 workgroups, each a contiguous range of row groups
-  uint32_t nparts = ceil_div(ngroups64 ? ngroups64 : 1, kThreads * 4);
-  if (nparts > NVFP4_AMAX_MAX_WG) nparts = NVFP4_AMAX_MAX_WG;
-  const uint32_t per_wg = ceil_div(ngroups64 ? ngroups64 : 1, nparts);
-  const bool rht = q.rht != 0;
+  const bool rht = q.rht != 0, sr = q.rounding == 1;
+  uint64_t help = kHelpTicks;
+  if (const char *e = getenv("NVFP4_HELP_DELAY_TICKS")) help = strtoull(e, nullptr, 10);
+  if (q.blocking == 0) {
+    const uint64_t ngroups64 = (uint64_t)q.rows * (uint64_t)(q.cols / 16);
+    const uint32_t ngroups = (uint32_t)ngroups64;
+    const uint32_t gpr = (uint32_t)(q.cols / 16);
+    const bool contig = (q.ld == q.cols);
+    if (!sr) {
+      const uint32_t nchunks = (uint32_t)quantize_chunks(q.rows, q.cols, 0, 0);
+#define NVFP4_Q1(R, C)                                                                      \
+  do {                                                                                      \
+    auto k = quant_1x16_kernel<R, C>;                                                       \
+    uint32_t grid = resident_grid(k, kT1);                                                  \
+    if (grid > nchunks) grid = nchunks;                                                     \
+    if (grid == 0) grid = 1;                                                                \
+    k<<<grid, kT1, 0, stream>>>(q.x, ngroups, gpr, q.ld, q.cols, q.rht_k0, q.rht_k1,        \
+                                q.sr_k0, q.sr_k1, q.sr_base, nchunks, help, q.ws,          \
+                                q.codes, q.scales, q.global_dec, q.dev_status);             \
+  } while (0)
+      if (rht) { if (contig) NVFP4_Q1(true, true); else NVFP4_Q1(true, false); }
+      else { if (contig) NVFP4_Q1(false, true); else NVFP4_Q1(false, false); }
+#undef NVFP4_Q1
+      return hipGetLastError();
+    }
+    // stochastic rounding: two passes, partials after the coordination block
+    uint32_t *partials = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(q.ws) + kCoordBytes);
+    uint32_t nparts = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, kThreads * 4);
+    if (nparts > kAmaxMaxWg) nparts = kAmaxMaxWg;
+    const uint32_t per_wg = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, nparts);
 #define NVFP4_AMAX(R, C)                                                                    \
   amax_kernel<R, C><<<nparts, kThreads, 0, stream>>>(q.x, ngroups, gpr, q.ld, q.rht_k0,    \
-                                                     q.rht_k1, per_wg, q.partials)
-  if (rht && contig) NVFP4_AMAX(true, true);
-  else if (rht) NVFP4_AMAX(true, false);
-  else if (contig) NVFP4_AMAX(false, true);
-  else NVFP4_AMAX(false, false);
+                                                     q.rht_k1, per_wg, partials)
+    if (rht) { if (contig) NVFP4_AMAX(true, true); else NVFP4_AMAX(true, false); }
+    else { if (contig) NVFP4_AMAX(false, true); else NVFP4_AMAX(false, false); }
 #undef NVFP4_AMAX
-
-  if (q.blocking == 0) {
-    const bool sr = q.rounding == 1;
-    // pass 2 grid: enough workgroups for 8 per CU, each a contiguous range of groups
-    uint32_t grid2 = ceil_div(ngroups64 ? ngroups64 : 1, kThreads);
-    if (grid2 > NVFP4_Q1_MAX_WG) grid2 = NVFP4_Q1_MAX_WG;
-    const uint32_t per_wg2 = ceil_div(ngroups64 ? ngroups64 : 1, grid2);
-    grid2 = ceil_div(ngroups64 ? ngroups64 : 1, per_wg2);
-#define NVFP4_Q1(R, S, C)                                                                   \
-  quant_1x16_kernel<R, S, C><<<grid2, kThreads, 0, stream>>>(                               \
+    uint32_t grid2 = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, kThreads);
+    if (grid2 > kSrMaxWg) grid2 = kSrMaxWg;
+    const uint32_t per_wg2 = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, grid2);
+    grid2 = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, per_wg2);
+#define NVFP4_QSR(R, C)                                                                     \
+  quant_1x16_sr_kernel<R, C><<<grid2, kThreads, 0, stream>>>(                               \
       q.x, ngroups, gpr, q.ld, q.cols, q.rht_k0, q.rht_k1, q.sr_k0, q.sr_k1, q.sr_base,     \
-      per_wg2, q.partials, nparts, q.codes, q.scales, q.global_dec, q.dev_status)
-    if (rht) {
-      if (sr) { if (contig) NVFP4_Q1(true, true, true); else NVFP4_Q1(true, true, false); }
-      else { if (contig) NVFP4_Q1(true, false, true); else NVFP4_Q1(true, false, false); }
-    } else {
-      if (sr) { if (contig) NVFP4_Q1(false, true, true); else NVFP4_Q1(false, true, false); }
-      else { if (contig) NVFP4_Q1(false, false, true); else NVFP4_Q1(false, false, false); }
-    }
-#undef NVFP4_Q1
+      per_wg2, partials, nparts, q.codes, q.scales, q.global_dec, q.dev_status)
+    if (rht) { if (contig) NVFP4_QSR(true, true); else NVFP4_QSR(true, false); }
+    else { if (contig) NVFP4_QSR(false, true); else NVFP4_QSR(false, false); }
+#undef NVFP4_QSR
+    return hipGetLastError();
   } else {
-    // one workgroup per block of 16 x 16 tiles
-    uint32_t grid = (uint32_t)(((q.rows / 16 + 15) / 16) * ((q.cols / 16 + 15) / 16));
-    if (grid == 0) grid = 1;   // an empty tensor still publishes its tensor scale
-    const bool sr = q.rounding == 1, tr = q.codes_t != nullptr;
+    const uint32_t nchunks = (uint32_t)quantize_chunks(q.rows, q.cols, 1, q.rounding);
+    const bool tr = q.codes_t != nullptr;
 #define NVFP4_Q16(S, T)                                                                     \
-  quant_16x16_kernel<S, T><<<grid, kThreads, 0, stream>>>(                                  \
-      q.x, q.rows, q.cols, q.ld, q.sr_k0, q.sr_k1, q.sr_base, q.partials, nparts, q.codes,  \
-      q.scales, q.codes_t, q.scales_t, q.global_dec, q.dev_status)
+  do {                                                                                      \
+    auto k = quant_16x16_kernel<S, T>;                                                      \
+    uint32_t grid = resident_grid(k, kT16);                                                 \
+    if (grid > nchunks) grid = nchunks;                                                     \
+    if (grid == 0) grid = 1;                                                                \
+    k<<<grid, kT16, 0, stream>>>(q.x, q.rows, q.cols, q.ld, q.sr_k0, q.sr_k1, q.sr_base,    \
+                                 nchunks, help, q.ws, q.codes, q.scales, q.codes_t,         \
+                                 q.scales_t, q.global_dec, q.dev_status);                   \
+  } while (0)
     if (sr) { if (tr) NVFP4_Q16(true, true); else NVFP4_Q16(true, false); }
     else { if (tr) NVFP4_Q16(false, true); else NVFP4_Q16(false, false); }
 #undef NVFP4_Q16

@@ -142,9 +142,34 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+_WORKSPACES = {}
+
+
+def new_workspace(device):
+    """A quantize workspace: nvfp4_quantize_workspace_bytes() bytes, zero-filled as the
+    library requires before first use."""
+    import torch
+    return torch.zeros(nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def _workspace(dev, stream_handle):
+    """One workspace per (device, stream): calls on one stream run in order, so they can
+    share it; calls on different streams never do."""
+    key = (dev.index, stream_handle)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = new_workspace(dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def quantize(x, blocking="1x16", rounding="rne", rht=False, rht_seed=0, sr_seed=0,
-             sr_index_base=0, with_transpose=False, stream=None, out=None) -> NVFP4Tensor:
-    """Quantize a 2-D bf16 CUDA tensor (row stride x.stride(0)) to NVFP4."""
+             sr_index_base=0, with_transpose=False, stream=None, out=None,
+             workspace=None) -> NVFP4Tensor:
+    """Quantize a 2-D bf16 CUDA tensor (row stride x.stride(0)) to NVFP4.
+
+    workspace: optional uint8 CUDA tensor from new_workspace(), used by one stream at a
+    time; by default one cached workspace per (device, stream) is used."""
     import torch
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
@@ -162,14 +187,13 @@ def quantize(x, blocking="1x16", rounding="rne", rht=False, rht_seed=0, sr_seed=
             ct = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
             st_ = torch.empty((cols // 16, rows // 16), dtype=torch.uint8, device=dev)
         out = NVFP4Tensor(codes, scales, g, rows, cols, blk, ct, st_, st)
-    ws_bytes = nvfp4_quantize_workspace_bytes()
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sh = _stream(stream, dev)
+    ws = workspace if workspace is not None else _workspace(dev, sh.value)
     prm = QuantParams(blk, _ROUNDING[rounding], 1 if rht else 0, 0, rht_seed, sr_seed,
                       sr_index_base)
     rc = nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), prm, _ptr(out.codes),
                         _ptr(out.scales), _ptr(out.global_dec), _ptr(out.codes_t),
-                        _ptr(out.scales_t), _ptr(out.status), _ptr(ws), ws_bytes,
-                        _stream(stream, dev))
+                        _ptr(out.scales_t), _ptr(out.status), _ptr(ws), ws.numel(), sh)
     if rc != NVFP4_OK:
         raise NVFP4Error(rc, "nvfp4_quantize")
     return out

@@ -91,8 +91,10 @@ typedef struct {
     int32_t reserved;         /* must be 0 */
 } nvfp4_operand;
 
-/* Bytes of scratch memory nvfp4_quantize needs (device memory, caller-allocated, contents
- * need no initialisation and are overwritten).  The same value for every shape. */
+/* Bytes of device memory nvfp4_quantize needs as its workspace (caller-allocated; the same
+ * value for every shape the ABI accepts).  The workspace carries coordination state from
+ * one call to the next: zero-fill it once before its first use and then leave it to the
+ * library.  A workspace serves one stream: calls that use it must not overlap in time. */
 size_t nvfp4_quantize_workspace_bytes(void);
 
 /*
@@ -115,8 +117,12 @@ size_t nvfp4_quantize_workspace_bytes(void);
  *             16x16 blocks these are exactly the transposed codes of x, so W and W^T come
  *             from one read ([PR] training stability section).  NULL to skip.
  * scales_t    (device, out) scales of x^T, cols/16 x rows/16; required iff codes_t is given.
- * dev_status  (device, out, optional) 0, or 1 if the input held inf or NaN.
- * workspace   (device) at least nvfp4_quantize_workspace_bytes() bytes.
+ * dev_status  (device, out, optional) 0; 1 if the input held inf or NaN; 2 if a wait
+ *             between workgroups passed its last-resort time limit (the results are then
+ *             invalid; this indicates a fault, not a property of the input).
+ * workspace   (device) at least nvfp4_quantize_workspace_bytes() bytes, zero-filled before
+ *             its first use (see nvfp4_quantize_workspace_bytes).  Calls captured in a
+ *             HIP graph may be replayed: each launch tags its state afresh.
  */
 nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                             const nvfp4_quant_params *p, uint8_t *codes, uint8_t *scales,

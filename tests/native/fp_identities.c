@@ -1,0 +1,82 @@
+/* Binary32 identities that the HIP kernels use as shortcuts, checked on the CPU.
+ *
+ *  1. div6:   for every binary32 a in [2^-125, FLT_MAX], the product q0 = a * RN(1/6)
+ *             corrected once by the exact FMA residual, fma(fma(-q0, 6, a), RN(1/6), q0),
+ *             equals the correctly rounded a / 6 (exhaustive).
+ *  2. absadd: for binary32 a, b: max(|RN(a + b)|, |RN(a - b)|) == RN(|a| + |b|)
+ *             (random pairs over the whole exponent range, zeros of both signs).
+ *  3. quarter: RN(RN(t / 4) * r) == RN(t * RN(r / 4)) when |t| >= 2^-124 and
+ *             r >= 2^-124, and both are below 2^-18 in magnitude, with the sign of t,
+ *             when |t| < 2^-124 and r < 2^108 (random pairs).
+ * Prints one line per identity: "<name> <checked> <mismatches>".  Built with
+ * -ffp-contract=off so that every operation rounds on its own. */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+static float f_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t u_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+static uint64_t splitmix(uint64_t *s) {
+  uint64_t z = (*s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* a finite binary32 with a uniformly random exponent field (0..254), mantissa, sign */
+static float rand_finite(uint64_t *s) {
+  uint64_t z = splitmix(s);
+  uint32_t e = (uint32_t)(z % 255u), m = (uint32_t)(z >> 8) & 0x7FFFFFu, sg = (uint32_t)(z >> 40) & 1u;
+  if (((z >> 48) & 63u) == 0) m = 0;          /* some exact powers of two and zeros */
+  if (((z >> 54) & 63u) == 0) { e = 0; m = 0; }
+  return f_of((sg << 31) | (e << 23) | m);
+}
+
+int main(void) {
+  const float c = 1.0f / 6.0f;
+  uint64_t bad = 0, n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+  for (int64_t ui = 0x01000000; ui < 0x7F800000; ++ui) {
+    const float a = f_of((uint32_t)ui);
+    const float q = a / 6.0f;
+    const float q0 = a * c;
+    const float r = fmaf(-q0, 6.0f, a);
+    const float q1 = fmaf(r, c, q0);
+    bad += u_of(q) != u_of(q1);
+    ++n;
+  }
+  printf("div6 %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+
+  bad = 0; n = 0;
+  uint64_t s = 12345;
+  for (int i = 0; i < 20000000; ++i) {
+    float a = rand_finite(&s), b = rand_finite(&s);
+    if (i % 7 == 0) b = f_of(u_of(a) ^ (uint32_t)(splitmix(&s) & 0x800000FFu));  /* near-equal pairs */
+    const float p = a + b, m = a - b;
+    const uint32_t lhs = u_of(fabsf(p)) > u_of(fabsf(m)) ? u_of(fabsf(p)) : u_of(fabsf(m));
+    const uint32_t rhs = u_of(fabsf(a) + fabsf(b));
+    bad += lhs != rhs;
+    ++n;
+  }
+  printf("absadd %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+
+  bad = 0; n = 0;
+  for (int i = 0; i < 20000000; ++i) {
+    float t = rand_finite(&s), r = fabsf(rand_finite(&s));
+    if (i & 1) t = f_of(u_of(t) & 0x82FFFFFFu);   /* push half of them toward tiny |t| */
+    const int tiny_t = fabsf(t) < 0x1p-124f;
+    if (r < 0x1p-124f || (tiny_t && r >= 0x1p108f)) continue;
+    const float y = (t * 0.25f) * r;
+    const float z = t * (r * 0.25f);
+    int ok;
+    if (!tiny_t) ok = u_of(y) == u_of(z);
+    else ok = fabsf(y) < 0x1p-18f && fabsf(z) < 0x1p-18f && ((u_of(y) ^ u_of(t)) >> 31) == 0 &&
+              ((u_of(z) ^ u_of(t)) >> 31) == 0;
+    bad += !ok;
+    ++n;
+  }
+  printf("quarter %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+  return 0;
+}

@@ -171,6 +171,65 @@ def test_w5_weight_full():
     assert np.array_equal(host(q.scales_t), ref[1].T)
 
 
+def test_more_chunks_than_resident_workgroups():
+    # 8192 x 8192 with RHT: 4.2M row groups, more 1x16 chunks than the GPU holds in
+    # registers, so some workgroups re-read the chunks they could not keep
+    say("1x16 RHT RNE 8192x8192: chunks re-read after the tensor scale")
+    x = W.normal_outliers(8192, 8192, seed=11)
+    kw = dict(rht=True, rht_seed=W.RHT_SEED)
+    assert_same(run_quant(x, **kw), oracle_quant(x, **kw))
+
+
+@pytest.fixture
+def help_at_once(monkeypatch):
+    # every waiting workgroup computes the partial maxima it has not seen yet itself
+    monkeypatch.setenv("NVFP4_HELP_DELAY_TICKS", "0")
+    yield
+
+
+def test_waiters_compute_missing_partials(help_at_once):
+    say("help path: waiters compute missing partial maxima themselves")
+    x = W.normal_outliers(2048, 5120, seed=12)
+    for kw in (dict(rht=True, rht_seed=3), dict()):
+        assert_same(run_quant(x, **kw), oracle_quant(x, **kw))
+    w = W.normal_scaled(2048, 1024, seed=13, std=0.02)
+    ref = oracle_quant(w, blocking="16x16")
+    q = run_quant(w, blocking="16x16", with_transpose=True)
+    assert_same(q, ref)
+    ref_t = oracle_quant(np.ascontiguousarray(w.T), blocking="16x16")
+    assert np.array_equal(host(q.codes_t), ref_t[0])
+    assert np.array_equal(host(q.scales_t), ref_t[1])
+
+
+def test_graph_replay():
+    # a captured quantize replayed on new data: every launch must tag its workspace state
+    # afresh, or a replay could take the previous replay's partial maxima for its own
+    say("HIP graph replay of quantize (1x16 RHT, 16x16 with W^T) on changing inputs")
+    xs = [W.normal_outliers(1024, 2048, seed=s) for s in (21, 22, 23)]
+    xs[1] = W.normal_scaled(1024, 2048, seed=24, std=0.001)   # a much smaller tensor amax
+    for kw in (dict(rht=True, rht_seed=5), dict(blocking="16x16", with_transpose=True)):
+        xd = to_dev(xs[0])
+        ws = N.new_workspace(xd.device)
+        q = N.quantize(xd, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=side):
+            N.quantize(xd, out=q, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        okw = {k: v for k, v in kw.items() if k != "with_transpose"}
+        for i in (1, 0, 2, 1, 1, 0):
+            xd.copy_(to_dev(xs[i]))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_same(q, oracle_quant(xs[i], **okw))
+            # eager work on the same workspace between replays
+            N.quantize(xd, out=q, workspace=ws, **kw)
+            torch.cuda.synchronize()
+            assert_same(q, oracle_quant(xs[i], **okw))
+
+
 def test_edge_values():
     say("edge values: zeros, -0, subnormal, huge, non-finite")
     z = np.zeros((32, 64), np.uint16)
@@ -192,6 +251,21 @@ def test_edge_values():
     tiny_amax[9, 30] = 0x8001
     for kw in (dict(), dict(rounding="sr"), dict(blocking="16x16")):
         assert_same(run_quant(tiny_amax, **kw), oracle_quant(tiny_amax, **kw))
+    # RHT with a tensor scale too large for the folded quarter (the multiplier table
+    # exceeds 2^108): the kernels scale every transformed value by 1/4 first
+    for kw in (dict(rht=True, rht_seed=5), dict(rht=True, rht_seed=5, rounding="sr", sr_seed=2)):
+        assert_same(run_quant(tiny_amax, **kw), oracle_quant(tiny_amax, **kw))
+    small = W.f32_to_bf16_bits(rng.standard_normal((64, 64)).astype(np.float32) * np.float32(1e-30))
+    pick = rng.random((64, 64)) < 0.3
+    small[pick] = sub[pick]
+    # normal-range tensor with bf16 subnormals inside its row groups: folded quarter,
+    # tiny transformed values round to zero codes with their sign
+    mixed = W.normal_outliers(64, 64, seed=6)
+    pick = rng.random((64, 64)) < 0.3
+    mixed[pick] = sub[pick]
+    for xin in (small, mixed):
+        for kw in (dict(rht=True, rht_seed=6), dict(rht=True, rht_seed=6, rounding="sr", sr_seed=3)):
+            assert_same(run_quant(xin, **kw), oracle_quant(xin, **kw))
     for bad in (0x7F80, 0xFF80, 0x7FC1):
         x = W.normal_outliers(32, 32, seed=3)
         x[7, 9] = bad
