@@ -119,15 +119,23 @@ def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
         xd = to_dev(x)
         nb = max(2, -(-nbuf_bytes // (xd.numel() * 2)))
         bufs = [xd] + [xd.clone() for _ in range(nb - 1)]
-        q = N.quantize(xd, **kw)
+        ws = N.new_workspace(xd.device)
+        q = N.quantize(xd, workspace=ws, **kw)
         for i in range(5):
-            N.quantize(bufs[i % nb], out=q, **kw)
+            N.quantize(bufs[i % nb], out=q, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        # the timed launches are replayed from a captured graph, so that the host's
+        # per-call cost (Python and ctypes) never leaves the GPU idle between kernels
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            for i in range(iters):
+                N.quantize(bufs[i % nb], out=q, workspace=ws, **kw)
+        g.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(iters):
-            N.quantize(bufs[i % nb], out=q, **kw)
+        g.replay()
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1000.0 / iters
@@ -136,7 +144,7 @@ def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
                      "frac": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": by,
                      "buffers": nb}
         log("micro %s: %.2f us, %.1f GB/s" % (name, us, by / us / 1e3))
-        del bufs, xd, q
+        del bufs, xd, q, g, ws
         torch.cuda.empty_cache()
     return res
 
