@@ -194,10 +194,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // Main path for K % 256 == 0.  One 256-thread workgroup per CU computes a 256 x 256 tile;
 // each wave owns 128 x 128 (4 x 4 MFMA blocks, 256 fp32 accumulators).  K advances 256
 // elements per step: every row of A and B contributes one 128-byte cache line of packed
-// codes and 16 scale bytes, which the direct global->LDS loads (global_load_lds_dwordx4)
+// codes and 16 scale bytes, which the direct global->LDS loads (buffer_load ... lds)
 // bring into one of two LDS stages while the waves compute on the other.  The 16-byte
-// chunks of a row are stored at slot (chunk ^ (row & 7)) so the MFMA-operand reads of 8
-// consecutive rows hit 8 different bank groups.
+// chunks of a row are stored at slot (chunk ^ ((row >> 1) & 7)): a 128-bit LDS read serves
+// 16 lanes (16 consecutive rows) per pass, and with 128-byte rows the 16 (row parity,
+// slot) pairs then cover the 64 banks once.  Scales are stored as [dword j][row] (4 bytes
+// per row per 64 K-elements), so the 32 rows a wave reads together are 32 consecutive
+// dwords.
 //
 // K mapping inside a step: lane half h reads chunk 2j + h (32 elements) for j = 0..3 and
 // feeds its 8-element pieces to four MFMAs; A and B use the same map.
@@ -258,8 +261,10 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc, (int64_t)p.N * rowb);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as, srows_a * kgroups);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs, srows_b * kgroups);
-  const int chunk = (lane & 7) ^ (lane >> 3);
-  const uint32_t voff_code = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk * 16);
+  // row 64w + 8i + lane/8 has swizzle key ((row >> 1) & 7) = 4 (i & 1) + lane/16
+  const int chunk_e = (lane & 7) ^ (lane >> 4), chunk_o = (lane & 7) ^ (4 + (lane >> 4));
+  const uint32_t voff_e = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk_e * 16);
+  const uint32_t voff_o = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk_o * 16);
   const int srow = 64 * wave + lane;   // scale rows: wave w loads tile rows 64w .. 64w+63
   const uint32_t voff_sa = (uint32_t)((p.a16 ? (srow >> 4) : srow) * kgroups);
   const uint32_t voff_sb = (uint32_t)((p.b16 ? (srow >> 4) : srow) * kgroups);
@@ -272,15 +277,22 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
     for (int i = 0; i < 8; ++i) {
       const uint32_t sa_off = __builtin_amdgcn_readfirstlane((uint32_t)((m0 + 8 * i) * rowb + kb * kRowB2));
       const uint32_t sb_off = __builtin_amdgcn_readfirstlane((uint32_t)((n0 + 8 * i) * rowb + kb * kRowB2));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + (8 * wave + i) * 1024, 16, voff_code,
+      const uint32_t voff = (i & 1) ? voff_o : voff_e;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + (8 * wave + i) * 1024, 16, voff,
                                                sa_off, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + kCodesB2 + (8 * wave + i) * 1024, 16,
-                                               voff_code, sb_off, 0, 0);
+                                               voff, sb_off, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, base + 2 * kCodesB2 + wave * 1024, 16, voff_sa,
-                                             __builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, base + 2 * kCodesB2 + kScalesB2 + wave * 1024, 16,
-                                             voff_sb, __builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16), 0, 0);
+    // scales: dword j of rows 64w .. 64w+63 to [j][row]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, base + 2 * kCodesB2 + j * 1024 + wave * 256, 4, voff_sa,
+          __builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16 + 4 * j), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, base + 2 * kCodesB2 + kScalesB2 + j * 1024 + wave * 256, 4, voff_sb,
+          __builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16 + 4 * j), 0, 0);
+    }
   };
 
   floatx16 acc[4][4];
@@ -303,15 +315,15 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   // chunk j of a stage: 16 code bytes per block row and the two scale bytes (K groups
   // 4j + 2h, 4j + 2h + 1) that cover them, into buffer j & 1
   auto load_chunk16 = [&](const uint8_t *st, int j) {
-    const int slot = ((2 * j + h) ^ (l32 & 7)) * 16;
+    const int slot = ((2 * j + h) ^ ((l32 >> 1) & 7)) * 16;
     const uint8_t *ssa = st + 2 * kCodesB2, *ssb = ssa + kScalesB2;
     const int b = j & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ca[b][i] = lds16(st + (wm * 128 + i * 32 + l32) * kRowB2 + slot);
       cb[b][i] = lds16(st + kCodesB2 + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
-      const uint32_t wa = *reinterpret_cast<const uint32_t *>(ssa + (wm * 128 + i * 32 + l32) * 16 + 4 * j);
-      const uint32_t wb = *reinterpret_cast<const uint32_t *>(ssb + (wn * 128 + i * 32 + l32) * 16 + 4 * j);
+      const uint32_t wa = *reinterpret_cast<const uint32_t *>(ssa + j * 1024 + (wm * 128 + i * 32 + l32) * 4);
+      const uint32_t wb = *reinterpret_cast<const uint32_t *>(ssb + j * 1024 + (wn * 128 + i * 32 + l32) * 4);
       hsa[b][i] = scale_pair(wa, h);
       hsb[b][i] = scale_pair(wb, h);
     }
@@ -367,15 +379,40 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }
   }
 
+  // Epilogue.  Accumulator element r of block (i, jj) sits at row 32 i + 8 (r / 4) + 4 h +
+  // r % 4 and column 32 jj + l32 of the wave's 128 x 128 block.  A tile wholly inside C
+  // takes the unchecked path: one row address per (i, r), the four column blocks as
+  // immediate offsets, bf16 by the hardware conversion (nearest-even; checked on every
+  // binary32 against the rounding of the guarded path below).
   const float alpha = (*p.ag) * (*p.bg);
+  const int rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + l32;
+  if (m0 + kT2 <= p.M && n0 + kT2 <= p.N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t off = (int64_t)(rbase + i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + cbase;
+        if (F32) {
+          float *dst = reinterpret_cast<float *>(p.c) + off;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) dst[jj * 32] = acc[i][jj][r] * alpha;
+        } else {
+          uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + off;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            dst[jj * 32] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][jj][r] * alpha));
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int col = n0 + wn * 128 + jj * 32 + l32;
+        const int row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        const int col = cbase + jj * 32;
         if (row < p.M && col < p.N) {
           const float v = acc[i][jj][r] * alpha;
           if (F32) {
