@@ -204,6 +204,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 //
 // K mapping inside a step: lane half h reads chunk 2j + h (32 elements) for j = 0..3 and
 // feeds its 8-element pieces to four MFMAs; A and B use the same map.
+typedef int v4i32 __attribute__((ext_vector_type(4)));
 constexpr int kT2 = 256;                 // tile rows (M) and columns (N)
 constexpr int kRowB2 = 128;              // packed bytes per row per K step (256 elements)
 constexpr int kCodesB2 = kT2 * kRowB2;   // 32 KB per operand per stage
@@ -252,46 +253,60 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   const int kgroups = p.K >> 4;
   const int nk = p.K / 256;
 
-  // DMA through bounds-checked buffer loads: a row past the end of an operand reads
-  // zeros (zero codes and zero scales contribute nothing; those rows are not stored).
-  // Instruction i of wave w fills LDS slots (8w + i) * 64 + lane, i.e. tile row
-  // 64w + 8i + lane/8, position lane%8, which holds chunk (lane%8) ^ (lane/8).
+  // Tiles travel through registers: bounds-checked 16-byte buffer loads (a row past the
+  // end of an operand reads zeros, and zero codes and scales contribute nothing; those
+  // rows are not stored) early in a K step, LDS writes after the stage barrier.  Load i
+  // of wave w covers tile row 64w + 8i + lane/8, natural chunk lane%8, which goes to
+  // slot chunk ^ ((row >> 1) & 7) = chunk ^ (4 (i & 1) + lane/16).  (The direct
+  // global->LDS load instructions were measured to cost ~250 cycles of issue each here.)
   const int64_t srows_a = p.a16 ? (p.M + 15) / 16 : p.M, srows_b = p.b16 ? (p.N + 15) / 16 : p.N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ac, (int64_t)p.M * rowb);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc, (int64_t)p.N * rowb);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as, srows_a * kgroups);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs, srows_b * kgroups);
-  // row 64w + 8i + lane/8 has swizzle key ((row >> 1) & 7) = 4 (i & 1) + lane/16
-  const int chunk_e = (lane & 7) ^ (lane >> 4), chunk_o = (lane & 7) ^ (4 + (lane >> 4));
-  const uint32_t voff_e = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk_e * 16);
-  const uint32_t voff_o = (uint32_t)((64 * wave + (lane >> 3)) * rowb + chunk_o * 16);
+  const int voff_code = (int)((64 * wave + (lane >> 3)) * rowb + (lane & 7) * 16);
+  const int wr_e = (lane >> 3) * kRowB2 + (((lane & 7) ^ (lane >> 4)) * 16);
+  const int wr_o = (lane >> 3) * kRowB2 + (((lane & 7) ^ (4 + (lane >> 4))) * 16);
   const int srow = 64 * wave + lane;   // scale rows: wave w loads tile rows 64w .. 64w+63
-  const uint32_t voff_sa = (uint32_t)((p.a16 ? (srow >> 4) : srow) * kgroups);
-  const uint32_t voff_sb = (uint32_t)((p.b16 ? (srow >> 4) : srow) * kgroups);
+  const int voff_sa = (int)((p.a16 ? (srow >> 4) : srow) * kgroups);
+  const int voff_sb = (int)((p.b16 ? (srow >> 4) : srow) * kgroups);
   const uint32_t soff_sa0 = (uint32_t)((p.a16 ? (m0 >> 4) : m0) * kgroups);
   const uint32_t soff_sb0 = (uint32_t)((p.b16 ? (n0 >> 4) : n0) * kgroups);
 
-  auto issue = [&](int kb, int stage) {
+  v4i32 sta[8], stb[8], ssa, ssb;   // one K step of this wave's share, in flight
+  // part q (0..3) of step kb: code rows 2q and 2q+1 of both operands, scales with q = 3
+  auto gload_part = [&](int kb, int q) {
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
+      const int sa_off = (int)__builtin_amdgcn_readfirstlane((uint32_t)((m0 + 8 * i) * rowb + kb * kRowB2));
+      const int sb_off = (int)__builtin_amdgcn_readfirstlane((uint32_t)((n0 + 8 * i) * rowb + kb * kRowB2));
+      sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_code, sa_off, 0);
+      stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff_code, sb_off, 0);
+    }
+    if (q == 3) {
+      ssa = __builtin_amdgcn_raw_buffer_load_b128(
+          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16), 0);
+      ssb = __builtin_amdgcn_raw_buffer_load_b128(
+          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16), 0);
+    }
+  };
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload_part(kb, q);
+  };
+  auto swrite = [&](int stage) {
     uint8_t *base = lds + stage * kStageB2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t sa_off = __builtin_amdgcn_readfirstlane((uint32_t)((m0 + 8 * i) * rowb + kb * kRowB2));
-      const uint32_t sb_off = __builtin_amdgcn_readfirstlane((uint32_t)((n0 + 8 * i) * rowb + kb * kRowB2));
-      const uint32_t voff = (i & 1) ? voff_o : voff_e;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + (8 * wave + i) * 1024, 16, voff,
-                                               sa_off, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + kCodesB2 + (8 * wave + i) * 1024, 16,
-                                               voff, sb_off, 0, 0);
+      uint8_t *rowp = base + (8 * wave + i) * 1024 + ((i & 1) ? wr_o : wr_e);
+      *reinterpret_cast<v4i32 *>(rowp) = sta[i];
+      *reinterpret_cast<v4i32 *>(rowp + kCodesB2) = stb[i];
     }
-    // scales: dword j of rows 64w .. 64w+63 to [j][row]
+    // scales: dword j of row r to [j][r]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, base + 2 * kCodesB2 + j * 1024 + wave * 256, 4, voff_sa,
-          __builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16 + 4 * j), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsb, base + 2 * kCodesB2 + kScalesB2 + j * 1024 + wave * 256, 4, voff_sb,
-          __builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16 + 4 * j), 0, 0);
+      reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + j * 1024)[srow] = ssa[j];
+      reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + kScalesB2 + j * 1024)[srow] = ssb[j];
     }
   };
 
@@ -342,12 +357,16 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   // Pipeline: chunk j of a K step is read from LDS four sub-steps before its first use;
   // the operands of sub-step s+1 are dequantized under the MFMAs of sub-step s.  The
   // stage barrier sits at sub-step 11, after the last LDS read of the current stage;
-  // past it the loads of step kb+2 go into the freed stage, chunk 0 of step kb+1 is read
-  // at sub-step 12 and its first operands prepared at sub-step 15.
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  // past it step kb+2 is written into the freed stage, chunk 0 of step kb+1 is read at
+  // sub-step 12 and its first operands prepared at sub-step 15.
+  gload(0);
+  swrite(0);
+  if (nk > 1) {
+    gload(1);
+    swrite(1);
+  }
+  if (nk > 2) gload(2);   // held in registers until stage 0 is free
   __syncthreads();
-  if (nk > 1) issue(1, 1);
   load_chunk16(lds, 0);
   dequant_step(0, ao[0], bo[0]);
   for (int kb = 0; kb < nk; ++kb) {
@@ -358,10 +377,11 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
       const int cur = s & 1;
       if ((s & 3) == 0 && s < 12) load_chunk16(st, (s >> 2) + 1);
       if (s == 11) {
-        __builtin_amdgcn_s_waitcnt(0);   // step kb+1 has landed; this wave is done with st
-        __syncthreads();
-        if (kb + 2 < nk) issue(kb + 2, kb & 1);
+        __syncthreads();   // every wave is done with st; step kb+1's writes are visible
+        if (kb + 2 < nk) swrite(kb & 1);
       }
+      // the registers are free again: step kb+3, one quarter per sub-step
+      if (s >= 12 && kb + 3 < nk) gload_part(kb + 3, s - 12);
       if (s == 12 && kb + 1 < nk) load_chunk16(st_next, 0);
       if (s + 1 < 16) dequant_step(s + 1, ao[cur ^ 1], bo[cur ^ 1]);
       else if (kb + 1 < nk) dequant_step(0, ao[0], bo[0]);
