@@ -294,20 +294,26 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) gload_part(kb, q);
   };
-  auto swrite = [&](int stage) {
+  // the part of the staged step that gload_part(., q) loaded
+  auto swrite_part = [&](int stage, int q) {
     uint8_t *base = lds + stage * kStageB2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
       uint8_t *rowp = base + (8 * wave + i) * 1024 + ((i & 1) ? wr_o : wr_e);
       *reinterpret_cast<v4i32 *>(rowp) = sta[i];
       *reinterpret_cast<v4i32 *>(rowp + kCodesB2) = stb[i];
     }
-    // scales: dword j of row r to [j][r]
+    if (q == 3) {   // scales: dword j of row r to [j][r]
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + j * 1024)[srow] = ssa[j];
-      reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + kScalesB2 + j * 1024)[srow] = ssb[j];
+      for (int j = 0; j < 4; ++j) {
+        reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + j * 1024)[srow] = ssa[j];
+        reinterpret_cast<int32_t *>(base + 2 * kCodesB2 + kScalesB2 + j * 1024)[srow] = ssb[j];
+      }
     }
+  };
+  auto swrite = [&](int stage) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) swrite_part(stage, q);
   };
 
   floatx16 acc[4][4];
@@ -376,11 +382,10 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
     for (int s = 0; s < 16; ++s) {
       const int cur = s & 1;
       if ((s & 3) == 0 && s < 12) load_chunk16(st, (s >> 2) + 1);
-      if (s == 11) {
-        __syncthreads();   // every wave is done with st; step kb+1's writes are visible
-        if (kb + 2 < nk) swrite(kb & 1);
-      }
-      // the registers are free again: step kb+3, one quarter per sub-step
+      if (s == 11) __syncthreads();   // every wave is done with st; step kb+1's writes are visible
+      // step kb+2 into the freed stage, one quarter per sub-step from 11 on; each quarter's
+      // registers then take the same quarter of step kb+3
+      if (s >= 11 && s < 15 && kb + 2 < nk) swrite_part(kb & 1, s - 11);
       if (s >= 12 && kb + 3 < nk) gload_part(kb + 3, s - 12);
       if (s == 12 && kb + 1 < nk) load_chunk16(st_next, 0);
       if (s + 1 < 16) dequant_step(s + 1, ao[cur ^ 1], bo[cur ^ 1]);
