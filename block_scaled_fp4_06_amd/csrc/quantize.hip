@@ -311,8 +311,10 @@ __device__ __forceinline__ float absmax16(const float v[16]) {
   return m;
 }
 
-// Output stores are streaming (non-temporal): nothing reads them back in the kernel, and
-// lines left dirty in L2 would otherwise be written back when the kernel ends.
+// Output stores of the 1x16 kernels are streaming (non-temporal): every store instruction
+// writes whole lines (consecutive row groups), nothing reads them back in the kernel, and
+// lines left dirty in L2 would otherwise be written back when the kernel ends.  The 16x16
+// kernel writes 32-byte row pieces, which L2 must merge: it uses ordinary stores.
 __device__ __forceinline__ void put2(uint8_t *p, uint2 v) {
   __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t *>(p));
   __builtin_nontemporal_store(v.y, reinterpret_cast<uint32_t *>(p) + 1);
@@ -648,8 +650,8 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
         uint2 q = encode16<SR>(v, rr, k);
         if (col_ok) {
-          put2(codes + row * (cols >> 1) + (int64_t)tc * 8, q);
-          if (r == 0) put1(scales + (size_t)trw * tpr + tc, sb);
+          *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
+          if (r == 0) scales[(size_t)trw * tpr + tc] = (uint8_t)sb;
         }
         if (TRANS) {
           transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
@@ -668,14 +670,14 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         if (ttc < tpr && c8 < nit) {
           const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTStride + c8 * 8);
           const int64_t trow = (int64_t)bc * 256 + j;
-          put2(codes_t + trow * (rows >> 1) + (int64_t)tr0 * 8 + c8 * 8, w);
+          *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr0 * 8 + c8 * 8) = w;
         }
       }
       // scales of x^T: row ttc (one per tile column), bytes [tr0, tr0 + nit)
       if (threadIdx.x < 16u * kG16) {
         const uint32_t tcl = threadIdx.x / kG16, it = threadIdx.x % kG16;
         const uint32_t ttc = bc * 16 + tcl;
-        if (ttc < tpr && it < nit) put1(scales_t + (size_t)ttc * tpc + tr0 + it, sbuf[tcl * kG16 + it]);
+        if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + tr0 + it] = sbuf[tcl * kG16 + it];
       }
     }
   };
