@@ -122,25 +122,28 @@ __device__ __forceinline__ uint32_t e2m1_rn_mag(float a) {
 }
 
 // Stochastic magnitude code of a >= 0 with the 16-bit random integer k: round up iff
-// (k + 1/2) / 2^16 < (a - lo) / (hi - lo).  Both sides are exact in binary32.
+// (k + 1/2) / 2^16 < (a - lo) / (hi - lo), evaluated as 2k + 1 < (a - lo) * 2^17 / step.
+// Every quantity is exact in binary32 (a - lo is exact, the step and 2^17 are powers of
+// two, 2k + 1 < 2^17), so both forms decide alike.  Below 1 the grid step is 1/2 (codes
+// 0, 1, 2); from 1 on, one mantissa bit is kept and the step is 2^(e-1) for a in
+// [2^e, 2^(e+1)).  (A branch-free form that computes both cases measured slower: whole
+// waves usually take one branch.)
 __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t k) {
   if (!(a < kE2M1Max)) return 7u;
   uint32_t lo_code;
-  float lo, inv_step;
+  float lo, inv17;
   if (a < 1.0f) {
     lo_code = (uint32_t)(a + a);            // truncation: 0 or 1
     lo = (float)lo_code * 0.5f;
-    inv_step = 2.0f;
+    inv17 = 262144.0f;                      // 2^17 / (1/2)
   } else {
     const uint32_t b = __float_as_uint(a);
     lo = __uint_as_float(b & 0xFFC00000u);  // truncate to 1 mantissa bit
-    lo_code = (b >> 22) - 252u;
-    // step = 2^(e-1); 1/step = 2^(1-e): exponent field 254 - efield + 1 ... built directly
-    inv_step = __uint_as_float((254u - ((b >> 23) & 0xFFu) + 1u) << 23);
+    lo_code = (b >> 22) - 252u;             // 1.0 -> code 2
+    // 2^17 / 2^(e-1) = 2^(18-e), from the exponent field E = e + 127
+    inv17 = __uint_as_float((272u - ((b >> 23) & 0xFFu)) << 23);
   }
-  const float frac = (a - lo) * inv_step;
-  const float u = ((float)k + 0.5f) * 1.52587890625e-05f;  // 2^-16
-  return lo_code + (u < frac ? 1u : 0u);
+  return lo_code + ((float)(2u * k + 1u) < (a - lo) * inv17 ? 1u : 0u);
 }
 
 // Nearest-even E2M1 codes of 16 values y[j] * rr, packed two per byte (element 2i in
