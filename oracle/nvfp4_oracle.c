@@ -278,8 +278,6 @@ int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
 {
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || ld_x < cols)
         return -1;
-    if (p->blocking == ORC_BLOCK_16x16 && p->rht)
-        return -2;
     if (p->rounding == ORC_ROUND_SR && (p->sr_index_base % 16))
         return -1;
 

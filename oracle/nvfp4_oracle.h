@@ -39,7 +39,9 @@ void orc_rht16(const float x[16], const float d[16], float y[16]);
 uint16_t orc_f32_to_bf16(float f);
 
 /* Returns 0 on success, 1 if the input held inf/NaN (global_dec = NaN, *status = 1,
- * codes and scales unspecified), -1 for a bad shape, -2 for RHT with 16x16 blocks. */
+ * codes and scales unspecified), -1 for a bad shape.  With rht the transform runs along
+ * each 16-element row group for either blocking (16x16 blocks then cover 16 transformed
+ * row groups). */
 int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                  const orc_params *p, uint8_t *codes, uint8_t *scales, float *global_dec,
                  uint32_t *status);

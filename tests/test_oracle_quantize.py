@@ -91,7 +91,7 @@ def test_scale_shapes_follow_micro_blocks(orc):
     assert wb["rows"] * wb["cols"] == wb["values_per_scale"]
 
 
-@pytest.mark.parametrize("blocking,rht", [(0, False), (0, True), (1, False)])
+@pytest.mark.parametrize("blocking,rht", [(0, False), (0, True), (1, False), (1, True)])
 def test_global_scale_reading(orc, blocking, rht):
     """s_dec = amax / (6 * 448): the block holding the tensor amax gets scale 448."""
     x = W.w1()
@@ -166,9 +166,36 @@ def test_bad_arguments(orc):
     with pytest.raises(orc.QuantizeError):
         orc.quantize(np.zeros((16, 24), np.uint16))
     with pytest.raises(orc.QuantizeError):
-        orc.quantize(np.zeros((16, 16), np.uint16), blocking=1, rht=True)
-    with pytest.raises(orc.QuantizeError):
         orc.quantize(np.zeros((16, 16), np.uint16), rounding=1, sr_index_base=8)
+
+
+def _rel(c, ref):
+    return float(np.linalg.norm(c - ref) / np.linalg.norm(ref))
+
+
+def test_rht_on_both_gemm_operands_keeps_the_product(orc):
+    """The random Hadamard transform keeps dot products (prism article, section on
+    outliers and rounding error): with the same sign vector applied to the K-groups of
+    both operands (1x16 activations, 16x16 weight), the NVFP4 product approximates X W as
+    well as the untransformed pair does; transforming one side only, or the two sides with
+    different sign vectors, does not approximate it at all."""
+    x = W.channel_outliers(64, 512, seed=31, nchan=4, factor=20.0)
+    w = W.normal_scaled(512, 96, seed=32, std=0.02)
+    wt = np.ascontiguousarray(w.T)
+    exact = W.bf16_bits_to_f32(x).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64)
+
+    def gemm(ka, kb):
+        ca, sa, ga, _ = orc.quantize(x, **ka)
+        cb, sb, gb, _ = orc.quantize(wt, blocking=orc.BLOCK_16x16, **kb)
+        return orc.gemm_reference((ca, sa, ga, 64, 512, 0), (cb, sb, gb, 96, 512, 1))
+
+    plain = _rel(gemm({}, {}), exact)
+    both = _rel(gemm(dict(rht=True, rht_seed=7), dict(rht=True, rht_seed=7)), exact)
+    one = _rel(gemm(dict(rht=True, rht_seed=7), {}), exact)
+    other = _rel(gemm(dict(rht=True, rht_seed=7), dict(rht=True, rht_seed=8)), exact)
+    assert plain < 0.2 and both < 0.2
+    assert both < 1.5 * plain
+    assert one > 0.8 and other > 0.4
 
 
 def test_sr_chunking_equals_whole(orc):
