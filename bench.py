@@ -106,7 +106,8 @@ class Timer:
 
 
 def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
-    """Standalone quantize of workloads 2-4 with rotated input buffers."""
+    """Standalone quantize of workloads 2-4 (and workload 2 with the RHT) with rotated
+    input buffers."""
     import torch
     res = {}
     cases = [
@@ -114,6 +115,9 @@ def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
         ("w3_rht_1x16_rne", W.w3(), dict(rht=True, rht_seed=W.RHT_SEED), "1x16", False),
         ("w4_rht_1x16_sr", W.w4(), dict(rht=True, rht_seed=W.RHT_SEED, rounding="sr", sr_seed=7),
          "1x16", False),
+        # weight with the activations' transform along K (both GEMM operands transformed)
+        ("w2_rht_16x16_wt", W.w2(), dict(blocking="16x16", with_transpose=True, rht=True,
+                                         rht_seed=W.RHT_SEED), "16x16", True),
     ]
     for name, x, kw, blk, tr in cases:
         xd = to_dev(x)

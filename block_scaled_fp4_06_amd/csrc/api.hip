@@ -37,7 +37,6 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
   if (p->rounding != NVFP4_ROUND_RNE && p->rounding != NVFP4_ROUND_STOCHASTIC)
     return NVFP4_ERR_UNSUPPORTED;
   if ((p->rht != 0 && p->rht != 1) || p->reserved != 0) return NVFP4_ERR_UNSUPPORTED;
-  if (p->rht && p->blocking == NVFP4_BLOCK_16x16) return NVFP4_ERR_UNSUPPORTED;
   if ((codes_t != nullptr) != (scales_t != nullptr)) return NVFP4_ERR_NULL;
   if (codes_t && p->blocking != NVFP4_BLOCK_16x16) return NVFP4_ERR_UNSUPPORTED;
   if (p->rounding == NVFP4_ROUND_STOCHASTIC && (p->sr_index_base & 15u)) return NVFP4_ERR_SHAPE;

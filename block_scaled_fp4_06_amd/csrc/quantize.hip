@@ -592,10 +592,11 @@ constexpr int kT16 = 256;
 constexpr int kG16 = 8;
 constexpr int kTStride = kG16 * 8 + 8;   // LDS bytes per staged x^T row (+8 against bank conflicts)
 
-template <bool SR, bool TRANS>
+template <bool RHT, bool SR, bool TRANS>
 __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sk0,
-    uint32_t sk1, uint64_t sr_base, uint32_t nchunks, uint64_t help, void *__restrict__ ws,
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t rk0,
+    uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base, uint32_t nchunks,
+    uint64_t help, void *__restrict__ ws,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
     uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTStride : 16];
@@ -611,6 +612,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   const uint32_t tpc = (uint32_t)(rows >> 4);          // tiles per tile-column
   const uint32_t cpr = (tpr + 15) >> 4;                // chunks per chunk-row
   const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
+  const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;   // transform along each lane's row group
   uint4 ra[kG16], rb[kG16];
 
   auto load_chunk = [&](uint32_t c) __attribute__((always_inline)) {
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
       rb[it] = mask4(p[1], m);
     });
   };
-  auto encode_chunk = [&](uint32_t c, const TensorScale &ts) __attribute__((always_inline)) {
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold) __attribute__((always_inline)) {
     const uint32_t br = c / cpr, bc = c - br * cpr;
     const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
     const uint32_t tc = bc * 16 + tl;
@@ -643,9 +645,15 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         const int64_t row = (int64_t)trw * 16 + r;
         float v[16];
         unpack16(ra[it], rb[it], v);
+        if (RHT) rht16_unscaled(v, sm);           // v = 4 y
         const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
-        const uint32_t sb = e4m3_encode(div6(__uint_as_float(tmax)) * ts.enc);
+        const float bmax = RHT ? __uint_as_float(tmax) * 0.25f : __uint_as_float(tmax);
+        const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
         const float rr = rtab[sb];
+        if (RHT && !fold) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+        }
         uint32_t k[16];
         if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
         uint2 q = encode16<SR>(v, rr, k);
@@ -685,6 +693,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   auto lane_max = [&](const uint4 &a, const uint4 &b) __attribute__((always_inline)) {
     float v[16];
     unpack16(a, b, v);
+    if (RHT) return rht16_absmax_bits(v, sm);
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
@@ -723,17 +732,18 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   wg_arrive<kT16>(hdr, tok);
 
   bool failed;
-  const uint32_t am = wg_amax<kT16>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  uint32_t am = wg_amax<kT16>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
   const TensorScale ts = tensor_scale(am);
   wg_publish_scale(failed, ts, global_dec, dev_status);
 
   if (ts.finite && !failed) {
-    build_rtab(rtab, ts.enc, false);
+    const bool fold = build_rtab(rtab, ts.enc, RHT);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
-      encode_chunk(last, ts);
+      encode_chunk(last, ts, fold);
       for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
         load_chunk(c);
-        encode_chunk(c, ts);
+        encode_chunk(c, ts, fold);
       }
     }
   }
@@ -822,18 +832,24 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
   } else {
     const uint32_t nchunks = (uint32_t)quantize_chunks(q.rows, q.cols, 1, q.rounding);
     const bool tr = q.codes_t != nullptr;
-#define NVFP4_Q16(S, T)                                                                     \
+#define NVFP4_Q16(R, S, T)                                                                  \
   do {                                                                                      \
-    auto k = quant_16x16_kernel<S, T>;                                                      \
+    auto k = quant_16x16_kernel<R, S, T>;                                                   \
     uint32_t grid = resident_grid(k, kT16);                                                 \
     if (grid > nchunks) grid = nchunks;                                                     \
     if (grid == 0) grid = 1;                                                                \
-    k<<<grid, kT16, 0, stream>>>(q.x, q.rows, q.cols, q.ld, q.sr_k0, q.sr_k1, q.sr_base,    \
-                                 nchunks, help, q.ws, q.codes, q.scales, q.codes_t,         \
-                                 q.scales_t, q.global_dec, q.dev_status);                   \
+    k<<<grid, kT16, 0, stream>>>(q.x, q.rows, q.cols, q.ld, q.rht_k0, q.rht_k1, q.sr_k0,    \
+                                 q.sr_k1, q.sr_base, nchunks, help, q.ws, q.codes,          \
+                                 q.scales, q.codes_t, q.scales_t, q.global_dec,             \
+                                 q.dev_status);                                             \
   } while (0)
-    if (sr) { if (tr) NVFP4_Q16(true, true); else NVFP4_Q16(true, false); }
-    else { if (tr) NVFP4_Q16(false, true); else NVFP4_Q16(false, false); }
+    if (rht) {
+      if (sr) { if (tr) NVFP4_Q16(true, true, true); else NVFP4_Q16(true, true, false); }
+      else { if (tr) NVFP4_Q16(true, false, true); else NVFP4_Q16(true, false, false); }
+    } else {
+      if (sr) { if (tr) NVFP4_Q16(false, true, true); else NVFP4_Q16(false, true, false); }
+      else { if (tr) NVFP4_Q16(false, false, true); else NVFP4_Q16(false, false, false); }
+    }
 #undef NVFP4_Q16
   }
   return hipGetLastError();

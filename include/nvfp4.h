@@ -72,8 +72,10 @@ typedef struct {
     int32_t rounding;       /* nvfp4_rounding: nearest-even, or stochastic ([NV-blog]
                                bullet 5; [PR] outliers-and-rounding section) */
     int32_t rht;            /* 1: apply the 16-point random Hadamard transform to every
-                               16-element row group before quantizing ([NV-blog] bullet 3);
-                               1x16 blocking only in this version */
+                               16-element row group before quantizing ([NV-blog] bullet 3),
+                               with either blocking.  Quantizing a GEMM's two K-contiguous
+                               operands with the same rht_seed keeps their product ([PR]
+                               outliers section: dot products are unchanged) */
     int32_t reserved;       /* must be 0 */
     uint64_t rht_seed;      /* selects the +-1 sign vector of the transform */
     uint64_t sr_seed;       /* Philox4x32-10 key for stochastic rounding */

@@ -76,7 +76,6 @@ def test_quantize_argument_errors(lib):
     assert q(P(0, 3, 0, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]
     assert q(P(0, 0, 2, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]
     assert q(P(0, 0, 0, 1, 0, 0, 0)) == ERR["UNSUPPORTED"]
-    assert q(P(1, 0, 1, 0, 0, 0, 0)) == ERR["UNSUPPORTED"]  # RHT with 16x16
     assert q(P(0, 1, 0, 0, 0, 0, 8)) == ERR["SHAPE"]        # SR base not a multiple of 16
     assert q(ct=FAKE) == ERR["NULL"]                         # codes_t without scales_t
     assert q(ct=FAKE, st=FAKE) == ERR["UNSUPPORTED"]         # transpose needs 16x16

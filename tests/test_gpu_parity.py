@@ -87,6 +87,10 @@ CASES = [
     (272, 528, "16x16", "rne", False),
     (1040, 2064, "1x16", "rne", True),
     (1040, 2064, "16x16", "sr", False),
+    # RHT with 16x16 blocks (the transform runs along each row group first)
+    (48, 80, "16x16", "rne", True),
+    (272, 528, "16x16", "sr", True),
+    (1040, 2064, "16x16", "rne", True),
 ]
 
 
@@ -199,6 +203,8 @@ def test_waiters_compute_missing_partials(help_at_once):
     ref_t = oracle_quant(np.ascontiguousarray(w.T), blocking="16x16")
     assert np.array_equal(host(q.codes_t), ref_t[0])
     assert np.array_equal(host(q.scales_t), ref_t[1])
+    kw = dict(blocking="16x16", rht=True, rht_seed=9)
+    assert_same(run_quant(w, **kw), oracle_quant(w, **kw))
 
 
 def test_graph_replay():
@@ -228,6 +234,43 @@ def test_graph_replay():
             N.quantize(xd, out=q, workspace=ws, **kw)
             torch.cuda.synchronize()
             assert_same(q, oracle_quant(xs[i], **okw))
+
+
+def test_w5_weight_rht_full():
+    # the weight transformed along K with the activations' sign vector (16x16 blocks, W^T
+    # emitted alongside): both GEMM operands carry the same transform
+    say("workload 5 weight, RHT along K + 16x16 RNE, with its transpose")
+    wt = np.ascontiguousarray(W.w5_weight().T)     # 20480 x 5120, K contiguous
+    kw = dict(blocking="16x16", rht=True, rht_seed=W.RHT_SEED)
+    ref = oracle_quant(wt, **kw)
+    q = run_quant(wt, with_transpose=True, **kw)
+    assert_same(q, ref)
+    c = ref[0]
+    full = np.empty((c.shape[0], c.shape[1] * 2), np.uint8)
+    full[:, 0::2], full[:, 1::2] = c & 0xF, c >> 4
+    ft = np.ascontiguousarray(full.T)
+    assert np.array_equal(host(q.codes_t), (ft[:, 0::2] | (ft[:, 1::2] << 4)).astype(np.uint8))
+    assert np.array_equal(host(q.scales_t), ref[1].T)
+
+
+def test_gemm_both_operands_transformed():
+    # X W with the same RHT on the K-groups of both operands: the GEMM kernel is the same;
+    # parity against the oracle, and the product approximates the untransformed one
+    say("GEMM with RHT on both operands (16x16 weight)")
+    M, N_, K = 512, 768, 1024
+    x = W.channel_outliers(M, K, seed=41)
+    w = W.normal_scaled(K, N_, seed=42, std=0.02)
+    wt = np.ascontiguousarray(w.T)
+    ka = dict(rht=True, rht_seed=W.RHT_SEED)
+    kb = dict(blocking="16x16", rht=True, rht_seed=W.RHT_SEED)
+    qa, qb = run_quant(x, **ka), run_quant(wt, **kb)
+    ra, rb = oracle_quant(x, **ka), oracle_quant(wt, **kb)
+    assert_same(qa, ra)
+    assert_same(qb, rb)
+    gemm_check(qa, qb, ra, rb, M, N_, K)
+    c = host(N.gemm(qa, qb, torch.float32)).astype(np.float64)
+    exact = W.bf16_bits_to_f32(x).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64)
+    assert np.linalg.norm(c - exact) / np.linalg.norm(exact) < 0.2
 
 
 def test_edge_values():
@@ -264,7 +307,8 @@ def test_edge_values():
     pick = rng.random((64, 64)) < 0.3
     mixed[pick] = sub[pick]
     for xin in (small, mixed):
-        for kw in (dict(rht=True, rht_seed=6), dict(rht=True, rht_seed=6, rounding="sr", sr_seed=3)):
+        for kw in (dict(rht=True, rht_seed=6), dict(rht=True, rht_seed=6, rounding="sr", sr_seed=3),
+                   dict(rht=True, rht_seed=6, blocking="16x16")):
             assert_same(run_quant(xin, **kw), oracle_quant(xin, **kw))
     for bad in (0x7F80, 0xFF80, 0x7FC1):
         x = W.normal_outliers(32, 32, seed=3)
