@@ -273,6 +273,28 @@ def test_gemm_both_operands_transformed():
     assert np.linalg.norm(c - exact) / np.linalg.norm(exact) < 0.2
 
 
+@pytest.mark.parametrize("name", ["w2", "w5_weight"])
+def test_weight_granularity_study(name):
+    # 1x16 against 16x16 blocks on the weights, through the GPU quantize and dequantize;
+    # the dequantized values are the oracle's bit for bit, so the errors are too
+    x = W.w2() if name == "w2" else W.w5_weight()
+    rows, cols = x.shape
+    xd = to_dev(x)
+    xf = torch.from_numpy(W.bf16_bits_to_f32(x)).cuda().double()
+    out = {}
+    for blk in ("1x16", "16x16"):
+        q = run_quant(x, blocking=blk, xdev=xd)
+        y = N.dequantize(q, torch.float32).double()
+        d = y - xf
+        out[blk] = (float(d.norm() / xf.norm()), float(d.abs().max()))
+        if name == "w2":
+            ref = oracle.dequantize(*oracle_quant(x, blocking=blk)[:3], rows, cols, BLK[blk])
+            assert np.array_equal(host(y.float()).view(np.uint32), ref.view(np.uint32))
+    say("granularity %s: rel-fro 1x16 %.4f 16x16 %.4f | max abs 1x16 %.3g 16x16 %.3g" % (
+        name, out["1x16"][0], out["16x16"][0], out["1x16"][1], out["16x16"][1]))
+    assert out["16x16"][0] > out["1x16"][0]
+
+
 def test_edge_values():
     say("edge values: zeros, -0, subnormal, huge, non-finite")
     z = np.zeros((32, 64), np.uint16)

@@ -198,6 +198,25 @@ def test_rht_on_both_gemm_operands_keeps_the_product(orc):
     assert one > 0.8 and other > 0.4
 
 
+def test_granularity_16x16_coarser_than_1x16(orc):
+    """One scale per 256 values is coarser than one per 16 (prism article, section on
+    training stability: 16x16 weight blocks trade precision for W / W^T consistency): on a
+    weight-like tensor the 16x16 round trip has the larger error, and every 16x16 scale is
+    at least the largest 1x16 scale of its 16 row groups."""
+    for x in (W.normal_scaled(512, 512, seed=51, std=0.02),
+              W.channel_outliers(512, 512, seed=52, nchan=8, factor=50.0)):
+        xf = W.bf16_bits_to_f32(x).astype(np.float64)
+        errs = []
+        for blk in (0, 1):
+            c, sc, g, _ = orc.quantize(x, blocking=blk)
+            y = orc.dequantize(c, sc, g, 512, 512, blocking=blk).astype(np.float64)
+            errs.append(np.linalg.norm(y - xf) / np.linalg.norm(xf))
+        assert errs[1] > errs[0]
+        s1 = orc.quantize(x, blocking=0)[1]
+        s16 = orc.quantize(x, blocking=1)[1]
+        assert np.array_equal(s16, s1.reshape(32, 16, 32).max(axis=1))
+
+
 def test_sr_chunking_equals_whole(orc):
     """Philox is keyed on (seed, element index): two half-tensors quantized with
     sr_index_base equal one call over the whole (same tensor amax in both halves)."""
