@@ -11,6 +11,10 @@ Functions and the passages they follow (the pages state the method in words):
     prism.simon-ai.net article 7890, sections "MVFP4格式的核心架构革新" (FP32 tensor
     scale over E4M3 block scales), "训练稳定性与敏感层保护策略" (16x16 weight blocks)
     and "应对异常值与舍入误差的技术手段" (random Hadamard transform, stochastic rounding).
+  * ``mx_quantize`` / ``mx_block_values_f64`` / ``mx_gemm_reference`` -- MXFP4, the
+    32-element power-of-two-scale format the prism article (section "MVFP4与MXFP4") and
+    10100.com (section 二(一)) set NVFP4 against; the scale rule is the OCP Microscaling
+    Formats v1.0 one (a reading: the pages give none).
   * ``gemm_reference`` -- the linear-layer product the recipe exists for (blog, same
     section, Figure 1 paragraph): the binary64 product of the exactly dequantized
     operands, computed with numpy's matmul (BLAS dgemm) as the one library step.
@@ -97,6 +101,12 @@ def lib():
         L.orc_rht_signs.argtypes = [u64, P]
         L.orc_rht16_rows_signs.argtypes = [P, i64, P, P]
         L.orc_abi_version.restype = ctypes.c_int
+        L.orc_mx_scale.argtypes = [ctypes.c_float]
+        L.orc_mx_scale.restype = ctypes.c_uint8
+        L.orc_mx_quantize.argtypes = [P, i64, i64, i64, P, P, P]
+        L.orc_mx_quantize.restype = ctypes.c_int
+        L.orc_mx_block_values_f64.argtypes = [P, P, i64, i64, P]
+        L.orc_mx_block_values_f64.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -249,6 +259,43 @@ def block_values_f64(codes, scales, rows, cols, blocking=BLOCK_1x16) -> np.ndarr
     if rc != 0:
         raise QuantizeError("bad shape")
     return out
+
+
+def mx_quantize(x_bf16: np.ndarray):
+    """MXFP4 quantize of a (rows, cols) bf16 tensor, cols % 32 == 0.
+
+    Returns (codes uint8 (rows, cols//2), scales uint8 E8M0 (rows, cols//32), status)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    st = np.zeros(1, dtype=np.uint32)
+    rc = lib().orc_mx_quantize(_p(x), rows, cols, cols, _p(codes), _p(scales), _p(st))
+    if rc < 0:
+        raise QuantizeError("oracle rejected the arguments (code %d)" % rc)
+    return codes, scales, int(st[0])
+
+
+def mx_scale(amax: float) -> int:
+    return int(lib().orc_mx_scale(float(amax)))
+
+
+def mx_block_values_f64(codes, scales, rows, cols) -> np.ndarray:
+    """Exact e2m1(q) * 2^(scale - 127) in binary64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.float64)
+    if lib().orc_mx_block_values_f64(_p(codes), _p(scales), rows, cols, _p(out)) != 0:
+        raise QuantizeError("bad shape")
+    return out
+
+
+def mx_gemm_reference(a, b, row_slice=None) -> np.ndarray:
+    """binary64 C = A . B^T for MXFP4 operands given as (codes, scales, rows, cols)."""
+    qa = mx_block_values_f64(*a)
+    if row_slice is not None:
+        qa = qa[row_slice]
+    return np.matmul(qa, mx_block_values_f64(*b).T)
 
 
 def gemm_reference(a, b, row_slice=None) -> np.ndarray:

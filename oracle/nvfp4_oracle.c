@@ -443,6 +443,98 @@ void orc_e4m3_encode_array(const float *s, int64_t n, uint8_t *out)
         out[i] = orc_e4m3_encode(s[i]);
 }
 
+/* ------------------------------------------------------------------------- */
+/* MXFP4: the 32-element, power-of-two-scale format the pages compare NVFP4 with  */
+/* ------------------------------------------------------------------------- */
+/* [PR] "MVFP4与MXFP4：通过缩放实现低精度推理" and [10100] section 二(一): MXFP4 keeps FP4 E2M1
+ * elements with one shared power-of-two (E8M0) scale per 32 elements; NVFP4 uses 16
+ * elements and an E4M3 scale.  The pages give no scale rule; READING: the OCP Microscaling
+ * Formats specification v1.0 (section 6.3): X = 2^(floor(log2(amax)) - emax) with emax = 2
+ * for E2M1 (largest value 6 = 1.5 * 2^2), the exponent clamped to the E8M0 range
+ * [-127, 127]; each element is v / X rounded to the nearest E2M1 value (ties to even),
+ * saturating at +-6.  A block holding inf or NaN gets the NaN scale 0xFF and zero codes.
+ * An all-zero block gets the smallest scale, 2^-127. */
+uint8_t orc_mx_scale(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;                       /* zero block: 2^-127 */
+    int e;
+    frexpf(amax, &e);                   /* amax = f * 2^e, f in [0.5, 1) */
+    int k = (e - 1) - 2;                /* floor(log2(amax)) - emax */
+    if (k < -127)
+        k = -127;
+    if (k > 127)
+        k = 127;
+    return (uint8_t)(k + 127);
+}
+
+double orc_mx_scale_value(uint8_t s)
+{
+    return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127);
+}
+
+/* codes: rows x cols/2 (element 2j in the low nibble), scales: rows x cols/32.  Returns
+ * 0, 1 if any block held inf/NaN, -1 for a bad shape (cols % 32 != 0). */
+int orc_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                    uint8_t *codes, uint8_t *scales, uint32_t *status)
+{
+    if (rows < 0 || cols < 0 || cols % 32 || ld_x < cols)
+        return -1;
+    int nonfinite = 0;
+    const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static) reduction(| : nonfinite)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float v[32];
+            float amax = 0.0f;
+            int bad = 0;
+            for (int j = 0; j < 32; ++j) {
+                v[j] = bf16_to_f32(x[r * ld_x + b * 32 + j]);
+                if (!isfinite(v[j]))
+                    bad = 1;
+                else if (fabsf(v[j]) > amax)
+                    amax = fabsf(v[j]);
+            }
+            uint8_t *cp = codes + r * (cols / 2) + b * 16;
+            if (bad) {
+                nonfinite = 1;
+                scales[r * nb + b] = 0xFF;
+                for (int j = 0; j < 16; ++j)
+                    cp[j] = 0;
+                continue;
+            }
+            const uint8_t s = orc_mx_scale(amax);
+            scales[r * nb + b] = s;
+            const int k = (int)s - 127;
+            for (int j = 0; j < 32; j += 2) {
+                /* v / X is a power-of-two scaling: exact unless it lands below the
+                 * binary32 normal range, where the value rounds to code 0 either way */
+                const uint8_t lo = orc_e2m1_encode_rn(ldexpf(v[j], -k));
+                const uint8_t hi = orc_e2m1_encode_rn(ldexpf(v[j + 1], -k));
+                cp[j / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    if (status)
+        *status = nonfinite ? 1u : 0u;
+    return nonfinite ? 1 : 0;
+}
+
+/* Exact element values e2m1(q) * X in binary64 (NaN for a NaN scale). */
+int orc_mx_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, double *out)
+{
+    if (rows < 0 || cols < 0 || cols % 32)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint8_t byte = codes[r * (cols / 2) + c / 2];
+            const uint8_t q = (c & 1) ? (byte >> 4) : (byte & 0xF);
+            out[r * cols + c] = (double)orc_e2m1_decode(q) *
+                                orc_mx_scale_value(scales[r * (cols / 32) + c / 32]);
+        }
+    return 0;
+}
+
 void orc_e2m1_encode_rn_array(const float *v, int64_t n, uint8_t *out)
 {
 #pragma omp parallel for schedule(static)

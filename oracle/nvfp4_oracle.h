@@ -50,6 +50,14 @@ int orc_dequantize(const uint8_t *codes, const uint8_t *scales, float global_dec
 int orc_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                          int64_t cols, int blocking, double *out);
 
+/* MXFP4 (32-element blocks, E8M0 scale; see the source for the rule). */
+uint8_t orc_mx_scale(float amax);
+double orc_mx_scale_value(uint8_t s);
+int orc_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                    uint8_t *codes, uint8_t *scales, uint32_t *status);
+int orc_mx_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, double *out);
+
 void orc_e4m3_encode_array(const float *s, int64_t n, uint8_t *out);
 void orc_e2m1_encode_rn_array(const float *v, int64_t n, uint8_t *out);
 void orc_e2m1_encode_sr_array(const float *v, const uint16_t *k, int64_t n, uint8_t *out);
