@@ -38,11 +38,29 @@ def hipcc() -> str:
 
 
 def build(out: str = LIB, extra=()) -> str:
+    """Compile every source to an object (in parallel, one hipcc per file), then link."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [
-        "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + sources()
-    subprocess.check_call(cmd, cwd=ROOT)
-    os.replace(tmp, out)
+    objs, procs = [], []
+    for src in sources():
+        obj = "%s.%d.o" % (out, len(objs))
+        objs.append(obj)
+        cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [
+            "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", obj, src]
+        procs.append((src, subprocess.Popen(cmd, cwd=ROOT)))
+    try:
+        for src, pr in procs:
+            if pr.wait() != 0:
+                raise subprocess.CalledProcessError(pr.returncode, "hipcc " + src)
+        subprocess.check_call([hipcc()] + HIPCC_FLAGS + list(extra) + ["-o", tmp] + objs,
+                              cwd=ROOT)
+        os.replace(tmp, out)
+    finally:
+        for pr in procs:
+            if pr[1].poll() is None:
+                pr[1].kill()
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

@@ -15,6 +15,8 @@ bool mult16(int64_t v) { return v >= 0 && (v & 15) == 0; }
 
 // Largest element count handled with 32-bit group indices.
 constexpr int64_t kMaxElems = (int64_t)1 << 35;
+// MXFP4 kernels index 8-element pieces with 32 bits.
+constexpr int64_t kMaxMxElems = (int64_t)1 << 34;
 
 nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
@@ -30,7 +32,8 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
                             uint32_t *dev_status, void *workspace, size_t workspace_bytes,
                             nvfp4_stream_t stream) {
   if (!p) return NVFP4_ERR_NULL;
-  if (!mult16(rows) || !mult16(cols) || ld_x < cols || rows * cols > kMaxElems)
+  if (!mult16(rows) || !mult16(cols) || ld_x < cols || rows > kMaxElems || cols > kMaxElems ||
+      rows * cols > kMaxElems)
     return NVFP4_ERR_SHAPE;
   if (p->blocking != NVFP4_BLOCK_1x16 && p->blocking != NVFP4_BLOCK_16x16)
     return NVFP4_ERR_UNSUPPORTED;
@@ -78,7 +81,8 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
                               const float *global_dec, int64_t rows, int64_t cols,
                               int32_t blocking, void *y, int64_t ld_y, int32_t out_dtype,
                               nvfp4_stream_t stream) {
-  if (!mult16(rows) || !mult16(cols) || ld_y < cols || rows * cols > kMaxElems)
+  if (!mult16(rows) || !mult16(cols) || ld_y < cols || rows > kMaxElems || cols > kMaxElems ||
+      rows * cols > kMaxElems)
     return NVFP4_ERR_SHAPE;
   if (blocking != NVFP4_BLOCK_1x16 && blocking != NVFP4_BLOCK_16x16) return NVFP4_ERR_UNSUPPORTED;
   if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_UNSUPPORTED;
@@ -130,6 +134,73 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
   g.out_f32 = out_dtype == NVFP4_OUT_FP32;
   g.c = c;
   return from_hip(nvfp4::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t *codes, uint8_t *scales, nvfp4_stream_t stream) {
+  if (rows < 0 || cols < 0 || (cols & 31) || ld_x < cols || rows > kMaxMxElems || cols > kMaxMxElems ||
+      rows * cols > kMaxMxElems)
+    return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;  // nothing to write
+  if (!x || !codes || !scales) return NVFP4_ERR_NULL;
+  if ((ld_x & 7) || !aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::MxQuantLaunch q;
+  q.x = x;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld = ld_x;
+  q.codes = codes;
+  q.scales = scales;
+  return from_hip(nvfp4::launch_mx_quantize(q, reinterpret_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                              int64_t cols, void *y, int64_t ld_y, int32_t out_dtype,
+                              nvfp4_stream_t stream) {
+  if (rows < 0 || cols < 0 || (cols & 31) || ld_y < cols || rows > kMaxMxElems || cols > kMaxMxElems ||
+      rows * cols > kMaxMxElems)
+    return NVFP4_ERR_SHAPE;
+  if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!codes || !scales || !y) return NVFP4_ERR_NULL;
+  if ((ld_y & 7) || !aligned16(codes) || !aligned16(scales) || !aligned16(y))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::MxDequantLaunch d;
+  d.codes = codes;
+  d.scales = scales;
+  d.rows = rows;
+  d.cols = cols;
+  d.ld_y = ld_y;
+  d.out_f32 = out_dtype == NVFP4_OUT_FP32;
+  d.y = y;
+  return from_hip(nvfp4::launch_mx_dequantize(d, reinterpret_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                        const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c,
+                        int64_t ldc, int32_t out_dtype, nvfp4_stream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || (K & 31) || ldc < N || M > (1 << 24) || N > (1 << 24) ||
+      K > (1 << 23))
+    return NVFP4_ERR_SHAPE;
+  if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!c || (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))) return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) ||
+      !aligned16(b_scales) || !aligned16(c))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::MxGemmLaunch g;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.b_codes = b_codes;
+  g.b_scales = b_scales;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldc = ldc;
+  g.out_f32 = out_dtype == NVFP4_OUT_FP32;
+  g.c = c;
+  return from_hip(nvfp4::launch_mx_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char *nvfp4_status_string(nvfp4_status s) {

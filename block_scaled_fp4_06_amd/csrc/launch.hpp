@@ -59,4 +59,31 @@ struct GemmLaunch {
 
 hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream);
 
+// MXFP4 (mxfp4.hip): 32-element blocks, one E8M0 scale byte each, no tensor scale.
+struct MxQuantLaunch {
+  const uint16_t *x;
+  int64_t rows, cols, ld;
+  uint8_t *codes, *scales;
+};
+
+hipError_t launch_mx_quantize(const MxQuantLaunch &q, hipStream_t stream);
+
+struct MxDequantLaunch {
+  const uint8_t *codes, *scales;
+  int64_t rows, cols, ld_y;
+  int out_f32;
+  void *y;
+};
+
+hipError_t launch_mx_dequantize(const MxDequantLaunch &d, hipStream_t stream);
+
+struct MxGemmLaunch {
+  const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+  int64_t M, N, K, ldc;
+  int out_f32;
+  void *c;
+};
+
+hipError_t launch_mx_gemm(const MxGemmLaunch &g, hipStream_t stream);
+
 }  // namespace nvfp4

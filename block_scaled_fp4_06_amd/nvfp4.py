@@ -46,7 +46,8 @@ class NVFP4Error(RuntimeError):
 
 
 EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
-            "nvfp4_gemm", "nvfp4_status_string", "nvfp4_abi_version")
+            "nvfp4_gemm", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
+            "nvfp4_status_string", "nvfp4_abi_version")
 
 _lib = None
 
@@ -71,6 +72,12 @@ def load(path: str = LIB_PATH):
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
                              P, i64, i32, P]
     L.nvfp4_gemm.restype = ctypes.c_int
+    L.mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P]
+    L.mxfp4_quantize.restype = ctypes.c_int
+    L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, i64, i32, P]
+    L.mxfp4_dequantize.restype = ctypes.c_int
+    L.mxfp4_gemm.argtypes = [P, P, P, P, i64, i64, i64, P, i64, i32, P]
+    L.mxfp4_gemm.restype = ctypes.c_int
     L.nvfp4_status_string.argtypes = [ctypes.c_int]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -99,6 +106,20 @@ def nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y, ld_y, o
 
 def nvfp4_gemm(a: Operand, b: Operand, M, N, K, c, ldc, out_dtype, stream) -> int:
     return int(load().nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, c, ldc,
+                                 out_dtype, stream))
+
+
+def mxfp4_quantize(x, rows, cols, ld_x, codes, scales, stream) -> int:
+    return int(load().mxfp4_quantize(x, rows, cols, ld_x, codes, scales, stream))
+
+
+def mxfp4_dequantize(codes, scales, rows, cols, y, ld_y, out_dtype, stream) -> int:
+    return int(load().mxfp4_dequantize(codes, scales, rows, cols, y, ld_y, out_dtype, stream))
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, c, ldc, out_dtype,
+               stream) -> int:
+    return int(load().mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, c, ldc,
                                  out_dtype, stream))
 
 
@@ -228,4 +249,62 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None):
                     _stream(stream, a.codes.device))
     if rc != NVFP4_OK:
         raise NVFP4Error(rc, "nvfp4_gemm")
+    return out
+
+
+# ------------------------------------------------------------------ MXFP4
+@dataclass
+class MXFP4Tensor:
+    """MXFP4 tensor: codes (rows, cols//2) uint8, scales (rows, cols//32) uint8 (E8M0)."""
+    codes: "object"
+    scales: "object"
+    rows: int
+    cols: int
+
+
+def mx_quantize(x, stream=None, out=None) -> MXFP4Tensor:
+    """Quantize a 2-D bf16 CUDA tensor (row stride x.stride(0)) to MXFP4."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        out = MXFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+                          rows, cols)
+    rc = mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(out.codes), _ptr(out.scales),
+                        _stream(stream, dev))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "mxfp4_quantize")
+    return out
+
+
+def mx_dequantize(q: MXFP4Tensor, out_dtype=None, stream=None, out=None):
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    rc = mxfp4_dequantize(_ptr(q.codes), _ptr(q.scales), q.rows, q.cols, _ptr(out),
+                          out.stride(0), od, _stream(stream, q.codes.device))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "mxfp4_dequantize")
+    return out
+
+
+def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=None, stream=None, out=None):
+    """C = A . B^T with A (M x K) and B (N x K) MXFP4 operands."""
+    import torch
+    if a.cols != b.cols:
+        raise ValueError("K mismatch: %d vs %d" % (a.cols, b.cols))
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    rc = mxfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), a.rows,
+                    b.rows, a.cols, _ptr(out), out.stride(0), od,
+                    _stream(stream, a.codes.device))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "mxfp4_gemm")
     return out

@@ -163,6 +163,55 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
                         int64_t K, void *c, int64_t ldc, int32_t out_dtype,
                         nvfp4_stream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * MXFP4: the format the pages compare NVFP4 with ([NV-blog] recipe section, bullets 1-2:
+ * 32-element blocks with a power-of-two E8M0 scale instead of 16 with E4M3; [PR]
+ * "MVFP4与MXFP4"), the block format gfx950's scaled FP4 matrix instructions consume.
+ * The pages do not say how the power of two is picked; these calls use the OCP
+ * Microscaling Formats v1.0 rule: X = 2^(floor(log2 amax) - 2) over the block's finite
+ * amax (2 = exponent of E2M1's largest value 6), clamped to [2^-127, 2^127], biased byte
+ * s = log2 X + 127 (an all-zero block gets s = 0); a block holding inf or NaN gets the NaN
+ * scale s = 0xFF and zero codes.  Element code = e2m1(x / X), nearest-even, saturating at
+ * +-6, keeping the sign (also of zero).  There is no tensor scale and no status output:
+ * a non-finite block is visible as its 0xFF scale.
+ *
+ * Storage: codes as for NVFP4 (rows x cols/2 bytes, column 2j in the low nibble); scales
+ * rows x cols/32 bytes, row-major, one per 32 consecutive elements of a row.  A value
+ * decodes as e2m1(code) * 2^(s - 127) (NaN if s = 0xFF).
+ * ---------------------------------------------------------------------------------- */
+
+/*
+ * mxfp4_quantize -- quantize a row-major bf16 tensor to MXFP4 (rule above).
+ * x       (device) bf16 bit patterns, rows x cols, row stride ld_x >= cols (multiple of 8).
+ * rows    >= 0; cols a multiple of 32; rows * cols <= 2^34.
+ * codes   (device, out) rows x cols/2 bytes.   scales (device, out) rows x cols/32 bytes.
+ */
+nvfp4_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t *codes, uint8_t *scales, nvfp4_stream_t stream);
+
+/*
+ * mxfp4_dequantize -- y = e2m1(code) * 2^(s - 127), exact in both output types (NaN for
+ * s = 0xFF; e2m1 6 with s >= 254 overflows to inf).
+ * codes, scales  (device) in the MXFP4 storage above.
+ * y       (device, out) rows x cols, row stride ld_y >= cols (multiple of 8), bf16 or float.
+ */
+nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                              int64_t cols, void *y, int64_t ld_y, int32_t out_dtype,
+                              nvfp4_stream_t stream);
+
+/*
+ * mxfp4_gemm -- C = A . B^T for MXFP4 operands on the native scaled FP4 matrix
+ * instructions, fp32 accumulation (the product of the NVFP4 GEMM, with 32-element E8M0
+ * blocks and no tensor scales).
+ *   C[m][n] = sum_k e2m1(A[m][k]) 2^(sA[m][k/32] - 127) * e2m1(B[n][k]) 2^(sB[n][k/32] - 127)
+ * a_codes, a_scales  (device) M x K operand.   b_codes, b_scales (device) N x K operand.
+ * M, N in [0, 2^24]; K a multiple of 32, at most 2^23.
+ * c       (device, out) M x N row-major, row stride ldc >= N (any), bf16 or float.
+ */
+nvfp4_status mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                        const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c,
+                        int64_t ldc, int32_t out_dtype, nvfp4_stream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *nvfp4_status_string(nvfp4_status s);
 

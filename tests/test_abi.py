@@ -29,7 +29,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b((?:nv|mx)fp4_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -126,6 +126,43 @@ def test_gemm_argument_errors(lib):
     assert gm(b=op(res=1)) == ERR["UNSUPPORTED"]
     assert gm(od=9) == ERR["UNSUPPORTED"]
     assert gm(M=0, a=op(codes=None, scales=None, g=None), c=None) == ERR["OK"]
+
+
+def test_mx_argument_errors(lib):
+    def q(x=FAKE, rows=32, cols=64, ld=64, codes=FAKE, scales=FAKE):
+        return N.mxfp4_quantize(x, rows, cols, ld, codes, scales, None)
+    assert q(x=None) == ERR["NULL"]
+    assert q(scales=None) == ERR["NULL"]
+    assert q(cols=48, ld=48) == ERR["SHAPE"]          # blocks are 32 elements
+    assert q(rows=-1) == ERR["SHAPE"]
+    assert q(ld=32) == ERR["SHAPE"]
+    assert q(ld=68) == ERR["ALIGN"]
+    assert q(codes=FAKE + 4) == ERR["ALIGN"]
+    assert q(rows=1 << 20, cols=1 << 15, ld=1 << 15) == ERR["SHAPE"]   # 2^35 elements
+    assert q(rows=0, x=None, codes=None, scales=None) == ERR["OK"]
+
+    def d(codes=FAKE, scales=FAKE, rows=32, cols=64, y=FAKE, ld=64, od=0):
+        return N.mxfp4_dequantize(codes, scales, rows, cols, y, ld, od, None)
+    assert d(codes=None) == ERR["NULL"]
+    assert d(y=None) == ERR["NULL"]
+    assert d(cols=16, ld=16) == ERR["SHAPE"]
+    assert d(ld=60) == ERR["SHAPE"]
+    assert d(ld=68) == ERR["ALIGN"]
+    assert d(od=3) == ERR["UNSUPPORTED"]
+    assert d(cols=0, codes=None, scales=None, y=None) == ERR["OK"]
+
+    def gm(ac=FAKE, as_=FAKE, bc=FAKE, bs=FAKE, M=32, N_=32, K=64, c=FAKE, ldc=32, od=0):
+        return N.mxfp4_gemm(ac, as_, bc, bs, M, N_, K, c, ldc, od, None)
+    assert gm(ac=None) == ERR["NULL"]
+    assert gm(bs=None) == ERR["NULL"]
+    assert gm(c=None) == ERR["NULL"]
+    assert gm(K=48) == ERR["SHAPE"]
+    assert gm(K=1 << 24) == ERR["SHAPE"]
+    assert gm(M=-1) == ERR["SHAPE"]
+    assert gm(ldc=16) == ERR["SHAPE"]
+    assert gm(as_=FAKE + 1) == ERR["ALIGN"]
+    assert gm(od=2) == ERR["UNSUPPORTED"]
+    assert gm(N_=0, ac=None, as_=None, bc=None, bs=None, c=None) == ERR["OK"]
 
 
 def test_python_wrapper_raises_when_library_missing(tmp_path, monkeypatch):
