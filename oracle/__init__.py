@@ -317,3 +317,43 @@ def gemm_reference(a, b, row_slice=None) -> np.ndarray:
     c = np.matmul(qa, qb.T)
     c *= float(np.float32(ga)) * float(np.float32(gb))
     return c
+
+
+# ------------------------------------------------------------------ linear layer
+# The three products of a linear layer Y = X W in training, each on quantized operands:
+# Fprop Y = X W, Dgrad dX = dY W^T, Wgrad dW = X^T dY (blog, recipe section: the matrix
+# products of linear layers are what FP4 accelerates, bullets 1-5 name the quantization
+# steps; prism article, training-stability section: the forward pass uses W and the
+# backward pass W^T, so weights take 16x16 blocks; outliers section: random Hadamard
+# transform, stochastic rounding of gradients).  Readings where the pages leave a choice:
+#   * X: 1x16 blocks, nearest-even; W: 16x16 blocks, nearest-even, one quantization for
+#     both Fprop (as W^T) and Dgrad (as W);
+#   * dY: 1x16 blocks, stochastic rounding (gradients); Dgrad draws with sr_seed, Wgrad's
+#     dY^T with sr_seed + 1;
+#   * the Hadamard transform goes on the Wgrad inputs only: X^T and dY^T along the token
+#     dimension M, with one seed for both, so their product is unchanged.  The weight's
+#     single quantization could not carry a transform along K for Fprop and along N for
+#     Dgrad at once.
+def linear_operands(x, w, dy, rht_seed: int, sr_seed: int):
+    """Quantized operands of the three products, as ``quantize`` tuples:
+    (X, W^T, W, dY, X^T, dY^T) for x (M, K), w (K, N), dy (M, N) bf16 bit patterns."""
+    x, w, dy = (np.ascontiguousarray(a, dtype=np.uint16) for a in (x, w, dy))
+    qx = quantize(x)
+    qwt = quantize(np.ascontiguousarray(w.T), blocking=BLOCK_16x16)
+    qw = quantize(w, blocking=BLOCK_16x16)
+    qdy = quantize(dy, rounding=ROUND_SR, sr_seed=sr_seed)
+    qxt = quantize(np.ascontiguousarray(x.T), rht=True, rht_seed=rht_seed)
+    qdyt = quantize(np.ascontiguousarray(dy.T), rounding=ROUND_SR, rht=True, rht_seed=rht_seed,
+                    sr_seed=sr_seed + 1)
+    return qx, qwt, qw, qdy, qxt, qdyt
+
+
+def linear_reference(x, w, dy, rht_seed: int, sr_seed: int, operands=None):
+    """binary64 (Y, dX, dW) of the quantized linear layer (steps above)."""
+    M, K = x.shape
+    N = w.shape[1]
+    qx, qwt, qw, qdy, qxt, qdyt = operands or linear_operands(x, w, dy, rht_seed, sr_seed)
+    y = gemm_reference((*qx[:3], M, K, BLOCK_1x16), (*qwt[:3], N, K, BLOCK_16x16))
+    dx = gemm_reference((*qdy[:3], M, N, BLOCK_1x16), (*qw[:3], K, N, BLOCK_16x16))
+    dw = gemm_reference((*qxt[:3], K, M, BLOCK_1x16), (*qdyt[:3], N, M, BLOCK_1x16))
+    return y, dx, dw
