@@ -44,7 +44,7 @@ def build(out: str = LIB, extra=()) -> str:
     for src in sources():
         obj = "%s.%d.o" % (out, len(objs))
         objs.append(obj)
-        cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [
+        cmd = [hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra) + [
             "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", obj, src]
         procs.append((src, subprocess.Popen(cmd, cwd=ROOT)))
     try:

@@ -203,6 +203,24 @@ nvfp4_status mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const u
   return from_hip(nvfp4::launch_mx_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_transpose_bf16(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint16_t *y, int64_t ld_y, nvfp4_stream_t stream) {
+  if (rows < 0 || cols < 0 || (rows & 7) || (cols & 7) || ld_x < cols || ld_y < rows ||
+      rows > kMaxElems || cols > kMaxElems || rows * cols > kMaxElems)
+    return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!x || !y) return NVFP4_ERR_NULL;
+  if ((ld_x & 7) || (ld_y & 7) || !aligned16(x) || !aligned16(y)) return NVFP4_ERR_ALIGN;
+  nvfp4::TransposeLaunch t;
+  t.x = x;
+  t.rows = rows;
+  t.cols = cols;
+  t.ld_x = ld_x;
+  t.y = y;
+  t.ld_y = ld_y;
+  return from_hip(nvfp4::launch_transpose_bf16(t, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char *nvfp4_status_string(nvfp4_status s) {
   switch (s) {
     case NVFP4_OK: return "ok";

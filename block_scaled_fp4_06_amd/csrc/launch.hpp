@@ -86,4 +86,13 @@ struct MxGemmLaunch {
 
 hipError_t launch_mx_gemm(const MxGemmLaunch &g, hipStream_t stream);
 
+struct TransposeLaunch {
+  const uint16_t *x;
+  int64_t rows, cols, ld_x;
+  uint16_t *y;
+  int64_t ld_y;
+};
+
+hipError_t launch_transpose_bf16(const TransposeLaunch &t, hipStream_t stream);
+
 }  // namespace nvfp4

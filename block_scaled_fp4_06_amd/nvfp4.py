@@ -46,7 +46,8 @@ class NVFP4Error(RuntimeError):
 
 
 EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
-            "nvfp4_gemm", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm",
+            "nvfp4_gemm", "nvfp4_transpose_bf16", "mxfp4_quantize", "mxfp4_dequantize",
+            "mxfp4_gemm",
             "nvfp4_status_string", "nvfp4_abi_version")
 
 _lib = None
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
                              P, i64, i32, P]
     L.nvfp4_gemm.restype = ctypes.c_int
+    L.nvfp4_transpose_bf16.argtypes = [P, i64, i64, i64, P, i64, P]
+    L.nvfp4_transpose_bf16.restype = ctypes.c_int
     L.mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P]
     L.mxfp4_quantize.restype = ctypes.c_int
     L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, i64, i32, P]
@@ -107,6 +110,10 @@ def nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y, ld_y, o
 def nvfp4_gemm(a: Operand, b: Operand, M, N, K, c, ldc, out_dtype, stream) -> int:
     return int(load().nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, c, ldc,
                                  out_dtype, stream))
+
+
+def nvfp4_transpose_bf16(x, rows, cols, ld_x, y, ld_y, stream) -> int:
+    return int(load().nvfp4_transpose_bf16(x, rows, cols, ld_x, y, ld_y, stream))
 
 
 def mxfp4_quantize(x, rows, cols, ld_x, codes, scales, stream) -> int:
@@ -249,6 +256,21 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None):
                     _stream(stream, a.codes.device))
     if rc != NVFP4_OK:
         raise NVFP4Error(rc, "nvfp4_gemm")
+    return out
+
+
+def transpose(x, stream=None, out=None):
+    """x^T of a 2-D bf16 CUDA tensor (unit column stride), contiguous."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
+    rc = nvfp4_transpose_bf16(_ptr(x), rows, cols, x.stride(0), _ptr(out), out.stride(0),
+                              _stream(stream, x.device))
+    if rc != NVFP4_OK:
+        raise NVFP4Error(rc, "nvfp4_transpose_bf16")
     return out
 
 

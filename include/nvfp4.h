@@ -163,6 +163,19 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
                         int64_t K, void *c, int64_t ldc, int32_t out_dtype,
                         nvfp4_stream_t stream);
 
+/*
+ * nvfp4_transpose_bf16 -- y = x^T for a bf16 tensor (bit patterns are moved, not changed).
+ * The weight-gradient GEMM of a linear layer contracts over the token dimension
+ * ([NV-blog] recipe section, bullet 3: the transform and the quantization apply to the GEMM
+ * inputs of the backward pass too), so X^T and dY^T are quantized along it: this call lays
+ * them out with that dimension contiguous.
+ * x     (device) rows x cols, row stride ld_x >= cols (multiple of 8).
+ * rows, cols  multiples of 8.
+ * y     (device, out) cols x rows, row stride ld_y >= rows (multiple of 8).
+ */
+nvfp4_status nvfp4_transpose_bf16(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint16_t *y, int64_t ld_y, nvfp4_stream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * MXFP4: the format the pages compare NVFP4 with ([NV-blog] recipe section, bullets 1-2:
  * 32-element blocks with a power-of-two E8M0 scale instead of 16 with E4M3; [PR]

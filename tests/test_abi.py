@@ -165,6 +165,20 @@ def test_mx_argument_errors(lib):
     assert gm(N_=0, ac=None, as_=None, bc=None, bs=None, c=None) == ERR["OK"]
 
 
+def test_transpose_argument_errors(lib):
+    def t(x=FAKE, rows=32, cols=64, ldx=64, y=FAKE, ldy=32):
+        return N.nvfp4_transpose_bf16(x, rows, cols, ldx, y, ldy, None)
+    assert t(x=None) == ERR["NULL"]
+    assert t(y=None) == ERR["NULL"]
+    assert t(rows=12) == ERR["SHAPE"]
+    assert t(cols=60, ldx=60) == ERR["SHAPE"]
+    assert t(ldx=32) == ERR["SHAPE"]
+    assert t(ldy=16) == ERR["SHAPE"]
+    assert t(ldx=68) == ERR["ALIGN"]
+    assert t(y=FAKE + 8) == ERR["ALIGN"]
+    assert t(rows=0, x=None, y=None) == ERR["OK"]
+
+
 def test_python_wrapper_raises_when_library_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(N, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
