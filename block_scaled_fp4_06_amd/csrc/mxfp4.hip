@@ -202,15 +202,15 @@ __device__ __forceinline__ void mx_mfma(floatx16 (&acc)[4][4], const v4i32 (&a)[
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
+// One 256 x 256 output tile (index `tile`) by the calling workgroup.
 template <bool F32, bool KFULL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mx_gemm_kernel(MxGemmParams p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kMStageB];
-
-  // tile order: the workgroups that one XCD (block id % 8) runs form a contiguous range
-  // of tiles, walked four tile-rows at a time so concurrent tiles share A and B
+__device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int tiles_m, int tiles_n,
+                                        uint8_t *lds) {
+  // tile order: the tiles whose index is congruent mod 8 (the workgroups of one XCD, which
+  // takes every eighth block) form a contiguous range, walked four tile-rows at a time
+  // so concurrent tiles share A and B
   const int G = tiles_m * tiles_n;
-  int bid = blockIdx.x;
+  int bid = tile;
   if ((G & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
   const int gm = 4;
   const int band = bid / (gm * tiles_n), in_band = bid - band * gm * tiles_n;
@@ -441,7 +441,36 @@ void mx_gemm_kernel(MxGemmParams p, int tiles_m, int tiles_n) {
   // Epilogue: element r of block (i, jj) is row 32 i + 8 (r / 4) + 4 h + r % 4, column
   // 32 jj + l32 of the wave's 128 x 128 block.  bf16 output rounds to nearest-even.
   const int rbase = m0 + wm * 128 + 4 * h, cbase = n0 + wn * 128 + l32;
-  if (m0 + kMT <= p.M && n0 + kMT <= p.N) {
+  const bool full = m0 + kMT <= p.M && n0 + kMT <= p.N;
+  if (!F32 && full && (p.ldc & 7) == 0) {
+    // bf16 through LDS: each wave stages its 128 x 128 block row-major (rows padded to
+    // 272 bytes, so the two lane halves, 4 rows apart, hit disjoint banks), then writes
+    // it back with one 16-byte store per lane per 4 rows: 32 stores instead of 256
+    // two-byte ones.
+    constexpr int kOutStride = 272;
+    __syncthreads();   // every wave is done with the stages
+    uint8_t *ob = lds + wave * (128 * kOutStride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          *reinterpret_cast<uint16_t *>(ob + row * kOutStride + (jj * 32 + l32) * 2) =
+              __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][r]);
+        }
+    const int crow = lane >> 4, cchunk = lane & 15;
+    uint16_t *cdst = reinterpret_cast<uint16_t *>(p.c) + (int64_t)(m0 + wm * 128 + crow) * p.ldc +
+                     n0 + wn * 128 + cchunk * 8;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const v4i32 v = *reinterpret_cast<const v4i32 *>(ob + (4 * t + crow) * kOutStride + cchunk * 16);
+      *reinterpret_cast<v4i32 *>(cdst + (int64_t)(4 * t) * p.ldc) = v;
+    }
+    return;
+  }
+  if (full) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -473,6 +502,13 @@ void mx_gemm_kernel(MxGemmParams p, int tiles_m, int tiles_n) {
           else reinterpret_cast<uint16_t *>(p.c)[off] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][r]);
         }
       }
+}
+
+template <bool F32, bool KFULL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mx_gemm_kernel(MxGemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kMStageB];
+  mx_tile<F32, KFULL>(p, blockIdx.x, tiles_m, tiles_n, lds);
 }
 
 uint32_t capped_grid(uint64_t items, uint32_t per_block, uint32_t cap) {
@@ -517,7 +553,8 @@ hipError_t launch_mx_gemm(const MxGemmLaunch &g, hipStream_t stream) {
   p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K; p.ldc = g.ldc; p.c = g.c;
   const int tm = (int)((g.M + kMT - 1) / kMT), tn = (int)((g.N + kMT - 1) / kMT);
   const bool kfull = g.K % 256 == 0;
-#define MX_GEMM(F, KF) mx_gemm_kernel<F, KF><<<tm * tn, 256, 0, stream>>>(p, tm, tn)
+  const int grid = tm * tn;
+#define MX_GEMM(F, KF) mx_gemm_kernel<F, KF><<<grid, 256, 0, stream>>>(p, tm, tn)
   if (g.out_f32) { if (kfull) MX_GEMM(true, true); else MX_GEMM(true, false); }
   else { if (kfull) MX_GEMM(false, true); else MX_GEMM(false, false); }
 #undef MX_GEMM
