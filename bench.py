@@ -10,7 +10,9 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.  The p
 JSON line carries the step throughput (GEMM FLOP per step / step time), per-kernel
 times from HIP events recorded on the launch stream, the roofline of the dominant
 kernel, standalone quantize figures for workloads 2-4 (input buffers rotated so the
-256 MB Infinity Cache cannot hold them), and the CPU oracle's rate on a bounded sample.
+256 MB Infinity Cache cannot hold them), the MXFP4 variant (quantize, and the GEMM on the
+native scaled FP4 MFMA), one linear-layer training step (Fprop, Dgrad, Wgrad), and the
+CPU oracle's rate on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-micro]
 """
@@ -153,6 +155,126 @@ def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
     return res
 
 
+def micro_mxfp4(N, W, nbuf_bytes=512 << 20, iters=30, gemm_iters=10):
+    """MXFP4 (32-element E8M0 blocks): quantize of workload 3 (rotated input buffers,
+    graph-replayed) and the workload-5 GEMM on the native scaled FP4 MFMA."""
+    import torch
+    res = {}
+    xd = to_dev(W.w3())
+    n = xd.numel()
+    nb = max(2, -(-nbuf_bytes // (n * 2)))
+    bufs = [xd] + [xd.clone() for _ in range(nb - 1)]
+    q = N.mx_quantize(xd)
+    for i in range(5):
+        N.mx_quantize(bufs[i % nb], out=q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for i in range(iters):
+            N.mx_quantize(bufs[i % nb], out=q)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / iters
+    by = 2 * n + n // 2 + n // 32
+    res["mx_quantize_w3"] = {"us": round(us, 2), "GBps": round(by / us / 1e3, 1),
+                             "frac": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": by,
+                             "buffers": nb}
+    log("micro mx_quantize_w3: %.2f us, %.1f GB/s" % (us, by / us / 1e3))
+    del bufs, g
+    wt = to_dev(np.ascontiguousarray(W.w5_weight().T))
+    qa, qb = N.mx_quantize(xd), N.mx_quantize(wt)
+    C = torch.empty((M, NN), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        N.mx_gemm(qa, qb, out=C)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(gemm_iters):
+        N.mx_gemm(qa, qb, out=C)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / gemm_iters
+    tf = 2.0 * M * NN * K / us / 1e6
+    res["mx_gemm_w5"] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
+                         "frac_mfma_fp4": round(tf / MFMA_FP4_PEAK_TFLOPS, 4)}
+    log("micro mx_gemm_w5: %.1f us, %.1f TFLOP/s" % (us, tf))
+    del xd, wt, qa, qb, C
+    torch.cuda.empty_cache()
+    return res
+
+
+def micro_linear(N, W, steps=5, warmup=2):
+    """One NVFP4 linear-layer training step at the workload-5 sizes: Fprop, Dgrad, Wgrad
+    with their quantizations and the two transposes of the Wgrad inputs."""
+    import torch
+    from block_scaled_fp4_06_amd import linear as L
+    x = to_dev(W.w3())
+    w = to_dev(W.w5_weight())
+    dy = to_dev(W.student_t(M, NN, seed=6))
+    for _ in range(warmup):
+        y, ctx = L.linear_forward(x, w)
+        L.linear_backward(dy, ctx)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd = bwd = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        y, ctx = L.linear_forward(x, w)
+        ev[1].record()
+        dx, dw = L.linear_backward(dy, ctx)
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd += ev[0].elapsed_time(ev[1])
+        bwd += ev[1].elapsed_time(ev[2])
+    fwd, bwd = fwd / steps, bwd / steps
+    flops = 3 * 2.0 * M * NN * K
+    res = {"ms_fwd": round(fwd, 3), "ms_bwd": round(bwd, 3),
+           "TFLOPs_step": round(flops / ((fwd + bwd) * 1e-3) / 1e12, 1)}
+    log("micro linear layer step: fwd %.3f ms, bwd %.3f ms" % (fwd, bwd))
+    del x, w, dy, y, ctx, dx, dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def context_scaled_mm_mx(N, W, iters=10):
+    """torch's scaled_mm (hipBLASLt) on MXFP4 operands from this library's quantizer, for
+    comparison with mxfp4_gemm on the same data; None where unsupported."""
+    import torch
+    import torch.nn.functional as F
+    try:
+        qa = N.mx_quantize(to_dev(W.w3()))
+        qb = N.mx_quantize(to_dev(np.ascontiguousarray(W.w5_weight().T)))
+        ST = getattr(F, "ScalingType", None) or F._ScalingType
+        SW = getattr(F, "SwizzleType", None) or F._SwizzleType
+        args = (qa.codes.view(torch.float4_e2m1fn_x2), qb.codes.view(torch.float4_e2m1fn_x2).t(),
+                qa.scales.view(torch.float8_e8m0fnu), ST.BlockWise1x32,
+                qb.scales.view(torch.float8_e8m0fnu), ST.BlockWise1x32, SW.NO_SWIZZLE,
+                SW.NO_SWIZZLE)
+
+        def call():
+            return F.scaled_mm(args[0], args[1], args[2], args[3], args[4], args[5], args[6],
+                               args[7], output_dtype=torch.bfloat16)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return round(2.0 * M * NN * K / (a.elapsed_time(b) / iters * 1e-3) / 1e12, 1)
+    except (RuntimeError, AttributeError, TypeError) as e:
+        log("scaled_mm MXFP4 unavailable: %s" % str(e)[:200])
+        return None
+
+
 def cpu_baseline(x_np, w_np, sample_rows=1024):
     """The oracle timed on this host on a bounded sample of one step (scaled to a step)."""
     import oracle
@@ -274,6 +396,10 @@ def main():
     if not args.no_micro:
         log("standalone quantize workloads")
         out["quantize"] = micro_quantize(N, W)
+        log("MXFP4 quantize and GEMM")
+        out["mxfp4"] = micro_mxfp4(N, W)
+        log("linear layer step (fwd + bwd)")
+        out["linear_step"] = micro_linear(N, W)
     if args.context:
         a16 = torch.randn((M, K), dtype=torch.float16, device="cuda")
         b16 = torch.randn((NN, K), dtype=torch.float16, device="cuda")
@@ -289,6 +415,8 @@ def main():
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 10
         out["context_torch_f16_matmul_TFLOPs"] = round(flops / (t * 1e-3) / 1e12, 1)
+        del a16, b16
+        out["context_torch_mxfp4_scaled_mm_TFLOPs"] = context_scaled_mm_mx(N, W)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
         out["cpu_baseline"] = cpu_baseline(x_np, w_np)
