@@ -109,7 +109,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
                         nvfp4_stream_t stream) {
   if (!a || !b) return NVFP4_ERR_NULL;
   if (!mult16(M) || !mult16(N) || !mult16(K) || ldc < N || M > (1 << 30) || N > (1 << 30) ||
-      K > (1 << 30))
+      K > (1 << 23))
     return NVFP4_ERR_SHAPE;
   if ((a->blocking != NVFP4_BLOCK_1x16 && a->blocking != NVFP4_BLOCK_16x16) ||
       (b->blocking != NVFP4_BLOCK_1x16 && b->blocking != NVFP4_BLOCK_16x16) || a->reserved ||

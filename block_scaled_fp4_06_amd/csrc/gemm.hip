@@ -259,35 +259,36 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   // of wave w covers tile row 64w + 8i + lane/8, natural chunk lane%8, which goes to
   // slot chunk ^ ((row >> 1) & 7) = chunk ^ (4 (i & 1) + lane/16).  (The direct
   // global->LDS load instructions were measured to cost ~250 cycles of issue each here.)
-  const int64_t srows_a = p.a16 ? (p.M + 15) / 16 : p.M, srows_b = p.b16 ? (p.N + 15) / 16 : p.N;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ac, (int64_t)p.M * rowb);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc, (int64_t)p.N * rowb);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as, srows_a * kgroups);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs, srows_b * kgroups);
+  // The resources start at the tile's first row and end at the operand's last, so offsets
+  // stay below 256 rows (32-bit for K < 2^24) however large the operands are.
+  const int rows_a = min(p.M - m0, kT2), rows_b = min(p.N - n0, kT2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)rows_a * rowb);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rows_b * rowb);
+  const int64_t s0a = p.a16 ? (m0 >> 4) : m0, s0b = p.b16 ? (n0 >> 4) : n0;
+  const int64_t snra = p.a16 ? (rows_a + 15) / 16 : rows_a, snrb = p.b16 ? (rows_b + 15) / 16 : rows_b;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as + s0a * kgroups, snra * kgroups);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs + s0b * kgroups, snrb * kgroups);
   const int voff_code = (int)((64 * wave + (lane >> 3)) * rowb + (lane & 7) * 16);
   const int wr_e = (lane >> 3) * kRowB2 + (((lane & 7) ^ (lane >> 4)) * 16);
   const int wr_o = (lane >> 3) * kRowB2 + (((lane & 7) ^ (4 + (lane >> 4))) * 16);
   const int srow = 64 * wave + lane;   // scale rows: wave w loads tile rows 64w .. 64w+63
   const int voff_sa = (int)((p.a16 ? (srow >> 4) : srow) * kgroups);
   const int voff_sb = (int)((p.b16 ? (srow >> 4) : srow) * kgroups);
-  const uint32_t soff_sa0 = (uint32_t)((p.a16 ? (m0 >> 4) : m0) * kgroups);
-  const uint32_t soff_sb0 = (uint32_t)((p.b16 ? (n0 >> 4) : n0) * kgroups);
 
   v4i32 sta[8], stb[8], ssa, ssb;   // one K step of this wave's share, in flight
   // part q (0..3) of step kb: code rows 2q and 2q+1 of both operands, scales with q = 3
   auto gload_part = [&](int kb, int q) {
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const int sa_off = (int)__builtin_amdgcn_readfirstlane((uint32_t)((m0 + 8 * i) * rowb + kb * kRowB2));
-      const int sb_off = (int)__builtin_amdgcn_readfirstlane((uint32_t)((n0 + 8 * i) * rowb + kb * kRowB2));
-      sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_code, sa_off, 0);
-      stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff_code, sb_off, 0);
+      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + kb * kRowB2));
+      sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_code, soff, 0);
+      stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff_code, soff, 0);
     }
     if (q == 3) {
       ssa = __builtin_amdgcn_raw_buffer_load_b128(
-          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane(soff_sa0 + kb * 16), 0);
+          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane((uint32_t)(kb * 16)), 0);
       ssb = __builtin_amdgcn_raw_buffer_load_b128(
-          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane(soff_sb0 + kb * 16), 0);
+          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane((uint32_t)(kb * 16)), 0);
     }
   };
   auto gload = [&](int kb) {

@@ -156,7 +156,7 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
  * a  (host struct, device pointers) M x K operand (activations; any blocking).
  * b  (host struct, device pointers) N x K operand, i.e. the transposed weight W^T (with
  *    16x16 blocks, the codes_t/scales_t of a K x N weight, or a weight quantized as N x K).
- * M, N, K  multiples of 16.
+ * M, N, K  multiples of 16; M, N <= 2^30, K <= 2^23.
  * c  (device, out) M x N row-major, row stride ldc >= N (multiple of 8), bf16 or float.
  */
 nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,

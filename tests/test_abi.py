@@ -118,6 +118,7 @@ def test_gemm_argument_errors(lib):
     assert gm(b=op(g=None)) == ERR["NULL"]
     assert gm(c=None) == ERR["NULL"]
     assert gm(K=40) == ERR["SHAPE"]
+    assert gm(K=1 << 24) == ERR["SHAPE"]
     assert gm(M=-16) == ERR["SHAPE"]
     assert gm(ldc=16) == ERR["SHAPE"]
     assert gm(ldc=36) == ERR["ALIGN"]

@@ -224,6 +224,32 @@ def test_mx_gemm_w5_full_sampled():
     mx_gemm_check(qa, qb, ra, rb, 8192, 20480, 5120, rows=rows)
 
 
+def test_mx_gemm_operand_beyond_2gib():
+    # A of 524800 x 8192 MXFP4 codes (2.15 GB): rows past the 2^31-byte mark are read
+    say("mx gemm with a 2.15 GB operand")
+    M, N_, K = 524800, 256, 8192
+    g = torch.Generator(device="cuda").manual_seed(2)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    asc = torch.randint(120, 134, (M, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    bc = torch.randint(0, 256, (N_, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    bsc = torch.randint(120, 134, (N_, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    c = N.mx_gemm(N.MXFP4Tensor(ac, asc, M, K), N.MXFP4Tensor(bc, bsc, N_, K), torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 262144, 524287, 524288, 524289, 524544, M - 1])
+    idx = torch.from_numpy(rows).cuda()
+    a64 = oracle.mx_block_values_f64(host(ac[idx]), host(asc[idx]), len(rows), K)
+    b64 = oracle.mx_block_values_f64(host(bc), host(bsc), N_, K)
+    ref = a64 @ b64.T
+    got = host(c[torch.from_numpy(rows).cuda()]).astype(np.float64)
+    e = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    say("  rel-fro %.3g" % e)
+    assert e <= 1e-3
+    bound = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 2.0 ** -24) * (np.abs(a64) @ np.abs(b64).T)
+    assert np.all(np.abs(got - ref) <= bound + 1e-37)
+    del ac, asc, c
+    torch.cuda.empty_cache()
+
+
 def test_format_comparison_on_gpu():
     # The pages' claim (16-element E4M3 blocks quantize more accurately than 32-element
     # E8M0 blocks), measured on the GPU path: per-block max error and relative Frobenius

@@ -469,6 +469,40 @@ def test_gemm_w5_full_sampled():
     gemm_check(qa, qw.transposed(), ref_a, ref_b, 8192, 20480, 5120, rows=rows)
 
 
+def test_gemm_operand_beyond_2gib():
+    # A of 524800 x 8192 (2.15 GB of codes): rows past the 2^31-byte mark must be read,
+    # not returned as zero by a clamped buffer range.  Codes and E4M3 scales are drawn
+    # directly (the GEMM is defined on any operand); sampled rows on both sides of the
+    # mark are checked against the oracle's binary64 product.
+    say("gemm with a 2.15 GB operand (524800 x 8192 codes)")
+    M, N_, K = 524800, 256, 8192
+    g = torch.Generator(device="cuda").manual_seed(1)
+    ac = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    asc = torch.randint(0x28, 0x48, (M, K // 16), dtype=torch.uint8, device="cuda", generator=g)
+    bc = torch.randint(0, 256, (N_, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    bsc = torch.randint(0x28, 0x48, (N_, K // 16), dtype=torch.uint8, device="cuda", generator=g)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    qa = N.NVFP4Tensor(ac, asc, one, M, K, 0)
+    qb = N.NVFP4Tensor(bc, bsc, one, N_, K, 0)
+    c = N.gemm(qa, qb, torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 131071, 262143, 262144, 393216, 524286, 524287, 524288, 524289,
+                     524290, 524543, 524544, 524700, M - 2, M - 1])   # 16: the oracle's unit
+    ra = host(ac[torch.from_numpy(rows).cuda()])
+    rsa = host(asc[torch.from_numpy(rows).cuda()])
+    a64 = oracle.block_values_f64(ra, rsa, len(rows), K, 0)
+    b64 = oracle.block_values_f64(host(bc), host(bsc), N_, K, 0)
+    ref = a64 @ b64.T
+    got = host(c[torch.from_numpy(rows).cuda()]).astype(np.float64)
+    e = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    bound = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 3 * 2.0 ** -24) * (np.abs(a64) @ np.abs(b64).T)
+    say("  rel-fro %.3g" % e)
+    assert e <= 1e-3
+    assert np.all(np.abs(got - ref) <= bound + 1e-37)
+    del ac, asc, c
+    torch.cuda.empty_cache()
+
+
 def test_sr_unbiased_64_seeds():
     """Workload 4 at 2048 x 5120: mean over 64 seeds of the stochastic codes equals the
     unrounded value (code units) -- z-test |mean z| <= 5 / sqrt(n)."""
