@@ -446,7 +446,9 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
     // bf16 through LDS: each wave stages its 128 x 128 block row-major (rows padded to
     // 272 bytes, so the two lane halves, 4 rows apart, hit disjoint banks), then writes
     // it back with one 16-byte store per lane per 4 rows: 32 stores instead of 256
-    // two-byte ones.
+    // two-byte ones.  The stores are non-temporal: C is written once and never read
+    // here, and keeping it out of the caches leaves them to the operands (measured
+    // ~10 % faster on the workload-5 product).
     constexpr int kOutStride = 272;
     __syncthreads();   // every wave is done with the stages
     uint8_t *ob = lds + wave * (128 * kOutStride);
@@ -466,7 +468,7 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const v4i32 v = *reinterpret_cast<const v4i32 *>(ob + (4 * t + crow) * kOutStride + cchunk * 16);
-      *reinterpret_cast<v4i32 *>(cdst + (int64_t)(4 * t) * p.ldc) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i32 *>(cdst + (int64_t)(4 * t) * p.ldc));
     }
     return;
   }
@@ -479,7 +481,7 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
         if (F32) {
           float *dst = reinterpret_cast<float *>(p.c) + off;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) dst[jj * 32] = acc[i][jj][r];
+          for (int jj = 0; jj < 4; ++jj) __builtin_nontemporal_store(acc[i][jj][r], dst + jj * 32);
         } else {
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + off;
 #pragma unroll
