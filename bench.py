@@ -107,9 +107,32 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
-def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
+def copy_bandwidth(nbuf_bytes=512 << 20, chunk=84 << 20, iters=30):
+    """Device-to-device copy rate (GB/s, read + write bytes) over rotated buffers: the
+    practical HBM ceiling the quantize rates are also compared with."""
+    import torch
+    nb = max(2, -(-nbuf_bytes // chunk))
+    src = [torch.empty(chunk, dtype=torch.uint8, device="cuda") for _ in range(nb)]
+    dst = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    for i in range(5):
+        dst.copy_(src[i % nb])
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        dst.copy_(src[i % nb])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / iters
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * chunk / us / 1e3, 1)
+
+
+def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30, reps=7, copy_gbps=None):
     """Standalone quantize of workloads 2-4 (and workload 2 with the RHT) with rotated
-    input buffers."""
+    input buffers; median and p10/p90 over `reps` replays of `iters` graph-captured calls."""
     import torch
     res = {}
     cases = [
@@ -138,24 +161,30 @@ def micro_quantize(N, W, nbuf_bytes=512 << 20, iters=30):
                 N.quantize(bufs[i % nb], out=q, workspace=ws, **kw)
         g.replay()
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1000.0 / iters
+        per = []
+        for _ in range(reps):   # each replay: the mean over `iters` calls
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1000.0 / iters)
+        p10, us, p90 = (float(v) for v in np.percentile(per, [10, 50, 90]))
         by = quant_bytes(x.shape[0], x.shape[1], blk, tr)
-        res[name] = {"us": round(us, 2), "GBps": round(by / us / 1e3, 1),
+        res[name] = {"us": round(us, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                     "GBps": round(by / us / 1e3, 1),
                      "frac": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": by,
                      "buffers": nb}
-        log("micro %s: %.2f us, %.1f GB/s" % (name, us, by / us / 1e3))
+        if copy_gbps:
+            res[name]["frac_copy"] = round(by / us / 1e3 / copy_gbps, 4)
+        log("micro %s: %.2f us (p10 %.2f, p90 %.2f), %.1f GB/s" % (name, us, p10, p90, by / us / 1e3))
         del bufs, xd, q, g, ws
         torch.cuda.empty_cache()
     return res
 
 
-def micro_mxfp4(N, W, nbuf_bytes=512 << 20, iters=30, gemm_iters=10):
+def micro_mxfp4(N, W, nbuf_bytes=512 << 20, iters=30, gemm_iters=10, copy_gbps=None):
     """MXFP4 (32-element E8M0 blocks): quantize of workload 3 (rotated input buffers,
     graph-replayed) and the workload-5 GEMM on the native scaled FP4 MFMA."""
     import torch
@@ -185,6 +214,8 @@ def micro_mxfp4(N, W, nbuf_bytes=512 << 20, iters=30, gemm_iters=10):
     res["mx_quantize_w3"] = {"us": round(us, 2), "GBps": round(by / us / 1e3, 1),
                              "frac": round(by / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes": by,
                              "buffers": nb}
+    if copy_gbps:
+        res["mx_quantize_w3"]["frac_copy"] = round(by / us / 1e3 / copy_gbps, 4)
     log("micro mx_quantize_w3: %.2f us, %.1f GB/s" % (us, by / us / 1e3))
     del bufs, g
     wt = to_dev(np.ascontiguousarray(W.w5_weight().T))
@@ -394,10 +425,13 @@ def main():
         out["copy_calibration_bytes"] = src.numel()
         del src, dst
     if not args.no_micro:
+        log("device copy reference")
+        cg = copy_bandwidth()
+        out["copy_GBps"] = cg
         log("standalone quantize workloads")
-        out["quantize"] = micro_quantize(N, W)
+        out["quantize"] = micro_quantize(N, W, copy_gbps=cg)
         log("MXFP4 quantize and GEMM")
-        out["mxfp4"] = micro_mxfp4(N, W)
+        out["mxfp4"] = micro_mxfp4(N, W, copy_gbps=cg)
         log("linear layer step (fwd + bwd)")
         out["linear_step"] = micro_linear(N, W)
     if args.context:
