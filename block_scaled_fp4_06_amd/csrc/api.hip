@@ -18,6 +18,12 @@ constexpr int64_t kMaxElems = (int64_t)1 << 35;
 // MXFP4 kernels index 8-element pieces with 32 bits.
 constexpr int64_t kMaxMxElems = (int64_t)1 << 34;
 
+// The GEMMs launch one workgroup per 128 x 128 (or larger) tile of C on a one-dimensional
+// grid, whose size is a 32-bit signed count.
+bool too_many_tiles(int64_t M, int64_t N) {
+  return ((M + 127) / 128) * ((N + 127) / 128) > (int64_t)0x7FFFFFFF;
+}
+
 nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
 }  // namespace
@@ -109,7 +115,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
                         nvfp4_stream_t stream) {
   if (!a || !b) return NVFP4_ERR_NULL;
   if (!mult16(M) || !mult16(N) || !mult16(K) || ldc < N || M > (1 << 30) || N > (1 << 30) ||
-      K > (1 << 23))
+      K > (1 << 23) || too_many_tiles(M, N))
     return NVFP4_ERR_SHAPE;
   if ((a->blocking != NVFP4_BLOCK_1x16 && a->blocking != NVFP4_BLOCK_16x16) ||
       (b->blocking != NVFP4_BLOCK_1x16 && b->blocking != NVFP4_BLOCK_16x16) || a->reserved ||
@@ -181,7 +187,7 @@ nvfp4_status mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const u
                         const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c,
                         int64_t ldc, int32_t out_dtype, nvfp4_stream_t stream) {
   if (M < 0 || N < 0 || K < 0 || (K & 31) || ldc < N || M > (1 << 24) || N > (1 << 24) ||
-      K > (1 << 23))
+      K > (1 << 23) || too_many_tiles(M, N))
     return NVFP4_ERR_SHAPE;
   if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return NVFP4_OK;

@@ -89,7 +89,7 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 sbd) {
 }
 
 template <bool F32, bool K32, bool HWCVT>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kLdsStride];
   __shared__ uint8_t sAs[kBM * 4], sBs[kBN * 4];
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  // one-dimensional grid (a y dimension would cap M at 65535 tiles)
+  const int m0 = (int)(blockIdx.x / tiles_n) * kBM, n0 = (int)(blockIdx.x % tiles_n) * kBN;
   const int64_t rowb = p.K >> 1;
   const int kgroups = p.K >> 4;
 
@@ -469,18 +470,19 @@ hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
     else gemm256_kernel<false><<<tm * tn, 256, 0, stream>>>(p, tm, tn);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
+  const int tiles_n = (int)((g.N + kBN - 1) / kBN);
+  const unsigned grid = (unsigned)(tiles_n * ((g.M + kBM - 1) / kBM));
   const bool k32 = (g.K % 32) == 0;
 #ifndef NVFP4_GEMM_HWCVT
 #define NVFP4_GEMM_HWCVT 1
 #endif
   constexpr bool hw = NVFP4_GEMM_HWCVT != 0;
   if (g.out_f32) {
-    if (k32) gemm_kernel<true, true, hw><<<grid, 256, 0, stream>>>(p);
-    else gemm_kernel<true, false, hw><<<grid, 256, 0, stream>>>(p);
+    if (k32) gemm_kernel<true, true, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
+    else gemm_kernel<true, false, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
   } else {
-    if (k32) gemm_kernel<false, true, hw><<<grid, 256, 0, stream>>>(p);
-    else gemm_kernel<false, false, hw><<<grid, 256, 0, stream>>>(p);
+    if (k32) gemm_kernel<false, true, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
+    else gemm_kernel<false, false, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
   }
   return hipGetLastError();
 }

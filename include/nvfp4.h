@@ -156,7 +156,8 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
  * a  (host struct, device pointers) M x K operand (activations; any blocking).
  * b  (host struct, device pointers) N x K operand, i.e. the transposed weight W^T (with
  *    16x16 blocks, the codes_t/scales_t of a K x N weight, or a weight quantized as N x K).
- * M, N, K  multiples of 16; M, N <= 2^30, K <= 2^23.
+ * M, N, K  multiples of 16; M, N <= 2^30, K <= 2^23, and at most 2^31 - 1 tiles of
+ *          128 x 128 in C.
  * c  (device, out) M x N row-major, row stride ldc >= N (multiple of 8), bf16 or float.
  */
 nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
@@ -218,7 +219,8 @@ nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64
  * blocks and no tensor scales).
  *   C[m][n] = sum_k e2m1(A[m][k]) 2^(sA[m][k/32] - 127) * e2m1(B[n][k]) 2^(sB[n][k/32] - 127)
  * a_codes, a_scales  (device) M x K operand.   b_codes, b_scales (device) N x K operand.
- * M, N in [0, 2^24]; K a multiple of 32, at most 2^23.
+ * M, N in [0, 2^24], at most 2^31 - 1 tiles of 128 x 128 in C; K a multiple of 32, at
+ * most 2^23.
  * c       (device, out) M x N row-major, row stride ldc >= N (any), bf16 or float.
  */
 nvfp4_status mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,

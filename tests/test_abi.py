@@ -119,6 +119,7 @@ def test_gemm_argument_errors(lib):
     assert gm(c=None) == ERR["NULL"]
     assert gm(K=40) == ERR["SHAPE"]
     assert gm(K=1 << 24) == ERR["SHAPE"]
+    assert gm(M=1 << 30, N_=1 << 30, ldc=1 << 30) == ERR["SHAPE"]   # 2^40 tiles of C
     assert gm(M=-16) == ERR["SHAPE"]
     assert gm(ldc=16) == ERR["SHAPE"]
     assert gm(ldc=36) == ERR["ALIGN"]
@@ -159,6 +160,7 @@ def test_mx_argument_errors(lib):
     assert gm(c=None) == ERR["NULL"]
     assert gm(K=48) == ERR["SHAPE"]
     assert gm(K=1 << 24) == ERR["SHAPE"]
+    assert gm(M=1 << 24, N_=1 << 24, ldc=1 << 24) == ERR["SHAPE"]   # 2^34 tiles of C
     assert gm(M=-1) == ERR["SHAPE"]
     assert gm(ldc=16) == ERR["SHAPE"]
     assert gm(as_=FAKE + 1) == ERR["ALIGN"]
