@@ -306,33 +306,41 @@ def context_scaled_mm_mx(N, W, iters=10):
         return None
 
 
-def cpu_baseline(x_np, w_np, sample_rows=1024):
-    """The oracle timed on this host on a bounded sample of one step (scaled to a step)."""
+def cpu_baseline(x_np, w_np, sample_rows=M, repeats=3):
+    """The oracle timed on this host: one step (quantize X and W with W^T, the binary64
+    GEMM, dequantize X) on `sample_rows` of the 8192 activation rows (all by default),
+    the rows' share scaled to a step; the median of `repeats` runs."""
     import oracle
     from block_scaled_fp4_06_amd import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     cores = min(threads, os.cpu_count() or 1)
     xs = np.ascontiguousarray(x_np[:sample_rows])
-    t0 = time.perf_counter()
-    ca, sa, ga, _ = oracle.quantize(xs, rht=True, rht_seed=W.RHT_SEED)
-    t1 = time.perf_counter()
-    cw, sw, gw, _ = oracle.quantize(w_np, blocking=oracle.BLOCK_16x16)
-    wt = np.ascontiguousarray(w_np.T)
-    cwt, swt, _, _ = oracle.quantize(wt, blocking=oracle.BLOCK_16x16)
-    t2 = time.perf_counter()
-    c = oracle.gemm_reference((ca, sa, ga, sample_rows, K, 0), (cwt, swt, gw, NN, K, 1))
-    t3 = time.perf_counter()
-    oracle.dequantize_bf16(ca, sa, ga, sample_rows, K)
-    t4 = time.perf_counter()
-    del c
-    scale = M / sample_rows
-    t_step = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale + (t4 - t3) * scale
+    steps, work = [], 0.0
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        ca, sa, ga, _ = oracle.quantize(xs, rht=True, rht_seed=W.RHT_SEED)
+        t1 = time.perf_counter()
+        cw, sw, gw, _ = oracle.quantize(w_np, blocking=oracle.BLOCK_16x16)
+        wt = np.ascontiguousarray(w_np.T)
+        cwt, swt, _, _ = oracle.quantize(wt, blocking=oracle.BLOCK_16x16)
+        t2 = time.perf_counter()
+        c = oracle.gemm_reference((ca, sa, ga, sample_rows, K, 0), (cwt, swt, gw, NN, K, 1))
+        t3 = time.perf_counter()
+        oracle.dequantize_bf16(ca, sa, ga, sample_rows, K)
+        t4 = time.perf_counter()
+        del c, wt
+        scale = M / sample_rows
+        steps.append((t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale + (t4 - t3) * scale)
+        work += t4 - t0
+    t_step = float(np.median(steps))
     flops = 2.0 * M * NN * K
+    what = ("the whole step (all %d activation rows)" % M if sample_rows == M else
+            "%d of %d activation rows, scaled to one step" % (sample_rows, M))
     return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": "%d of %d activation rows quantized, GEMM'd (binary64) and dequantized, "
-                      "full weight quantized (W and W^T); times scaled to one step; "
-                      "%.1f s of CPU work" % (sample_rows, M, t4 - t0),
+            "sample": "%s: quantize X (RHT, 1x16), quantize W and W^T (16x16), binary64 GEMM, "
+                      "dequantize X; median of %d runs, %.1f s of CPU work in all"
+                      % (what, repeats, work),
             "seconds_per_step_est": round(t_step, 2)}
 
 
