@@ -212,17 +212,6 @@ constexpr int kCodesB2 = kT2 * kRowB2;   // 32 KB per operand per stage
 constexpr int kScalesB2 = kT2 * 16;      // 4 KB per operand per stage
 constexpr int kStageB2 = 2 * kCodesB2 + 2 * kScalesB2;
 
-// Raw buffer resource over `bytes` bytes at p (reads past the end return zero).  Every
-// field is made wave-uniform so the descriptor lives in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF));
-  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
-                                           0x00020000);
-}
-
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 __device__ __forceinline__ half2_t scale_pair(uint32_t w, int h) {
@@ -263,12 +252,12 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   // The resources start at the tile's first row and end at the operand's last, so offsets
   // stay below 256 rows (32-bit for K < 2^24) however large the operands are.
   const int rows_a = min(p.M - m0, kT2), rows_b = min(p.N - n0, kT2);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)rows_a * rowb);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rows_b * rowb);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)rows_a * rowb);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rows_b * rowb);
   const int64_t s0a = p.a16 ? (m0 >> 4) : m0, s0b = p.b16 ? (n0 >> 4) : n0;
   const int64_t snra = p.a16 ? (rows_a + 15) / 16 : rows_a, snrb = p.b16 ? (rows_b + 15) / 16 : rows_b;
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.as + s0a * kgroups, snra * kgroups);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.bs + s0b * kgroups, snrb * kgroups);
+  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(p.as + s0a * kgroups, snra * kgroups);
+  const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(p.bs + s0b * kgroups, snrb * kgroups);
   const int voff_code = (int)((64 * wave + (lane >> 3)) * rowb + (lane & 7) * 16);
   const int wr_e = (lane >> 3) * kRowB2 + (((lane & 7) ^ (lane >> 4)) * 16);
   const int wr_o = (lane >> 3) * kRowB2 + (((lane & 7) ^ (4 + (lane >> 4))) * 16);

@@ -169,17 +169,6 @@ struct MxGemmParams {
   void *c;
 };
 
-// Raw buffer resource over `bytes` bytes at p (reads past the end return zero), with
-// every field wave-uniform so the descriptor sits in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void *p, int64_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF));
-  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
-                                           0x00020000);
-}
-
 __device__ __forceinline__ v8i32 widen(v4i32 a) {
   // FP4 operands occupy the first four registers of the 8-register operand
   return __builtin_shufflevector(a, (v4i32){0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -229,11 +218,11 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
   // Buffer resources start at the tile's first row and end at the operand's last, so a
   // row past M or N reads zero codes and zero scale bytes and adds nothing.
   const int ra_rows = min(p.M - m0, kMT), rb_rows = min(p.N - n0, kMT);
-  const __amdgpu_buffer_rsrc_t ra = mx_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)ra_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rb = mx_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rb_rows * rowb);
-  const __amdgpu_buffer_rsrc_t rsa = mx_rsrc(p.as + (int64_t)m0 * sgr, (int64_t)ra_rows * sgr);
-  const __amdgpu_buffer_rsrc_t rsb = mx_rsrc(p.bs + (int64_t)n0 * sgr, (int64_t)rb_rows * sgr);
-  const __amdgpu_buffer_rsrc_t r0 = mx_rsrc(p.ac, 0);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)ra_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rb_rows * rowb);
+  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(p.as + (int64_t)m0 * sgr, (int64_t)ra_rows * sgr);
+  const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(p.bs + (int64_t)n0 * sgr, (int64_t)rb_rows * sgr);
+  const __amdgpu_buffer_rsrc_t r0 = buffer_rsrc(p.ac, 0);
 
   // Load i (0..7) of wave w brings tile row 64 w + 8 i + lane / 8, chunk lane % 8, which
   // goes to slot chunk ^ ((row >> 1) & 7) = chunk ^ (4 (i & 1) + lane / 16).  Scales: lane

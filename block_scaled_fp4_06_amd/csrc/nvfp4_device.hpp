@@ -182,6 +182,19 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return Philox4{c0, c1, c2, c3};
 }
 
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer resource over `bytes` bytes at p: loads past the end return zero (clamped to
+// 2^31 - 1 bytes; callers base it where the 32-bit offsets stay below that).  Every field is
+// made wave-uniform so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int64_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           0x00020000);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -60,9 +60,16 @@ def linear_backward(dy, ctx: LinearContext, dx_dtype=None, dw_dtype=None, stream
     return dx, dw
 
 
+_AUTOGRAD_FN = None
+
+
 def autograd_linear():
     """A torch.autograd.Function running the layer's three products on NVFP4 operands
-    (bf16 in and out).  Built on first use so that importing the package needs no torch."""
+    (bf16 in and out).  Built once, on first use, so that importing the package needs no
+    torch."""
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is not None:
+        return _AUTOGRAD_FN
     import torch
 
     class NVFP4LinearFn(torch.autograd.Function):
@@ -77,4 +84,5 @@ def autograd_linear():
             dx, dw = linear_backward(dy.contiguous(), fctx.lin, dw_dtype=torch.bfloat16)
             return dx, dw, None, None
 
+    _AUTOGRAD_FN = NVFP4LinearFn
     return NVFP4LinearFn
