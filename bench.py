@@ -306,7 +306,7 @@ def context_scaled_mm_mx(N, W, iters=10):
         return None
 
 
-def cpu_baseline(x_np, w_np, sample_rows=M, repeats=3):
+def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
     """The oracle timed on this host: one step (quantize X and W with W^T, the binary64
     GEMM, dequantize X) on `sample_rows` of the 8192 activation rows (all by default),
     the rows' share scaled to a step; the median of `repeats` runs."""
