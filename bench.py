@@ -334,6 +334,23 @@ def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
         work += t4 - t0
     t_step = float(np.median(steps))
     flops = 2.0 * M * NN * K
+    # the activation quantize alone, on one thread and on all of them (GB/s by the
+    # algorithmic bytes of the sample)
+    rates = {}
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        xq = np.ascontiguousarray(x_np[:1024])
+        by = quant_bytes(1024, K, "1x16")
+        for n in (1, threads):
+            gomp.omp_set_num_threads(n)
+            t0 = time.perf_counter()
+            oracle.quantize(xq, rht=True, rht_seed=W.RHT_SEED)
+            rates["quantize_x_GBps_%d_thread%s" % (n, "" if n == 1 else "s")] = round(
+                by / (time.perf_counter() - t0) / 1e9, 3)
+        gomp.omp_set_num_threads(threads)
+    except OSError:
+        pass
     what = ("the whole step (all %d activation rows)" % M if sample_rows == M else
             "%d of %d activation rows, scaled to one step" % (sample_rows, M))
     return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
@@ -341,7 +358,7 @@ def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
             "sample": "%s: quantize X (RHT, 1x16), quantize W and W^T (16x16), binary64 GEMM, "
                       "dequantize X; median of %d runs, %.1f s of CPU work in all"
                       % (what, repeats, work),
-            "seconds_per_step_est": round(t_step, 2)}
+            "seconds_per_step_est": round(t_step, 2), **rates}
 
 
 def main():
