@@ -272,3 +272,25 @@ def test_format_comparison_on_gpu():
             "of 32-blocks" % (name, fro_nv, fro_mx, 100 * better))
         assert fro_nv < fro_mx
         assert better > 0.5
+
+
+def test_format_comparison_gemm_error():
+    # The same comparison at the product: the workload-5 GEMM (activations 8192 x 5120 with
+    # channel outliers, the 5120 x 20480 weight) in NVFP4 (1x16 activations, 16x16 weight)
+    # and in MXFP4, each against the exact product of the bf16 inputs on sampled rows.
+    say("formats at the product: workload-5 GEMM error, NVFP4 vs MXFP4")
+    x = W.w3()
+    w = W.w5_weight()
+    wt = np.ascontiguousarray(w.T)
+    xd, wd, wtd = to_dev(x), to_dev(w), to_dev(wt)
+    rows = np.sort(np.random.default_rng(9).choice(8192, 64, replace=False))
+    idx = torch.from_numpy(rows).cuda()
+    exact = W.bf16_bits_to_f32(x[rows]).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64)
+    qx = N.quantize(xd)
+    qw = N.quantize(wd, blocking="16x16", with_transpose=True)
+    c_nv = host(N.gemm(qx, qw.transposed(), torch.float32)[idx]).astype(np.float64)
+    c_mx = host(N.mx_gemm(N.mx_quantize(xd), N.mx_quantize(wtd), torch.float32)[idx]).astype(np.float64)
+    e_nv = np.linalg.norm(c_nv - exact) / np.linalg.norm(exact)
+    e_mx = np.linalg.norm(c_mx - exact) / np.linalg.norm(exact)
+    say("  GEMM rel-fro error vs the exact bf16 product: nvfp4 %.4f, mxfp4 %.4f" % (e_nv, e_mx))
+    assert e_nv < e_mx
