@@ -110,6 +110,17 @@ def test_quantize_row_stride():
     for kw in (dict(rht=True, rht_seed=3), dict(rounding="sr", sr_seed=5),
                dict(blocking="16x16", rounding="sr", sr_seed=6)):
         assert_same(run_quant(None, xdev=view, **kw), oracle_quant(x, **kw))
+    # 16x16 with the W^T output, with and without the transform: W^T's codes and scales
+    # are the transposes of W's
+    for kw in (dict(blocking="16x16"), dict(blocking="16x16", rht=True, rht_seed=4)):
+        q = run_quant(None, xdev=view, with_transpose=True, **kw)
+        ref = oracle_quant(x, **kw)
+        assert_same(q, ref)
+        full = np.empty((64, 160), np.uint8)
+        full[:, 0::2], full[:, 1::2] = ref[0] & 0xF, ref[0] >> 4
+        ft = np.ascontiguousarray(full.T)
+        assert np.array_equal(host(q.codes_t), (ft[:, 0::2] | (ft[:, 1::2] << 4)).astype(np.uint8))
+        assert np.array_equal(host(q.scales_t), np.ascontiguousarray(ref[1].T))
 
 
 def test_w1_full():
