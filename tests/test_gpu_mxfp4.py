@@ -294,3 +294,32 @@ def test_format_comparison_gemm_error():
     e_mx = np.linalg.norm(c_mx - exact) / np.linalg.norm(exact)
     say("  GEMM rel-fro error vs the exact bf16 product: nvfp4 %.4f, mxfp4 %.4f" % (e_nv, e_mx))
     assert e_nv < e_mx
+
+
+def test_mx_gemm_edge_blocks_and_strided_output():
+    # K = 288 (a partial last step of 32 elements), a non-finite block inside that partial
+    # step, all-zero blocks, and C written into a wider row-strided buffer
+    say("mx gemm edge blocks: partial last K step with a NaN block, zero blocks, strided C")
+    M, N_, K = 96, 80, 288
+    a = W.normal_scaled(M, K, seed=21, std=1.0)
+    b = W.normal_scaled(N_, K, seed=22, std=0.1)
+    a[7, 270] = 0x7FC0          # NaN in the last 32-element block of row 7
+    a[9, :] = 0                 # a zero row (every scale byte 0)
+    b[3, 32:64] = 0x8000        # a block of -0 in B
+    qa, qb = mx_run(a), mx_run(b)
+    ra, rb = assert_mx_same(qa, a), assert_mx_same(qb, b)
+    full = torch.full((M, N_ + 24), 5.0, dtype=torch.float32, device="cuda")
+    N.mx_gemm(qa, qb, out=full[:, :N_])
+    torch.cuda.synchronize()
+    c = host(full)
+    assert np.all(c[:, N_:] == 5.0)
+    cref = oracle.mx_gemm_reference((ra[0], ra[1], M, K), (rb[0], rb[1], N_, K))
+    got = c[:, :N_]
+    assert np.array_equal(np.isnan(got), np.isnan(cref))
+    assert np.all(np.isnan(got[7]))
+    assert np.all(got[9] == 0)
+    ok = ~np.isnan(cref)
+    qa64 = oracle.mx_block_values_f64(ra[0], ra[1], M, K)
+    qb64 = oracle.mx_block_values_f64(rb[0], rb[1], N_, K)
+    bound = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 2.0 ** -24) * (np.nan_to_num(np.abs(qa64)) @ np.abs(qb64).T) + 1e-37
+    assert np.all(np.abs(got[ok] - cref[ok]) <= bound[ok])
