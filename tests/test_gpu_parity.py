@@ -514,6 +514,34 @@ def test_gemm_operand_beyond_2gib():
     torch.cuda.empty_cache()
 
 
+def test_quantize_input_beyond_4gib():
+    # 65600 x 32768 bf16 (4.3 GB, 2^31 + 2M elements), RHT + 1x16: input offsets pass
+    # 2^32 bytes.  |x| <= 1 everywhere except one planted 100, whose transformed group holds
+    # the tensor amax, so the oracle run on that row plus sampled rows (1x16 blocks: a row's
+    # codes depend only on the tensor scale) reproduces the GPU's rows exactly.
+    say("quantize a 4.3 GB input (65600 x 32768, RHT, 1x16)")
+    rows, cols = 65600, 32768
+    g = torch.Generator(device="cuda").manual_seed(3)
+    xd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 8192):   # in slabs, to bound the fp32 temporary
+        r1 = min(rows, r0 + 8192)
+        xd[r0:r1] = (torch.randn((r1 - r0, cols), device="cuda", generator=g) * 0.2).clamp_(-1, 1).to(torch.bfloat16)
+    xd[40000, 12345] = 100.0
+    q = N.quantize(xd, rht=True, rht_seed=W.RHT_SEED)
+    torch.cuda.synchronize()
+    sample = np.array([40000, 0, 1, 16383, 32767, 49151, 65519, 65534, 65535, 65536, 65537,
+                       65550, 65570, 65590, rows - 2, rows - 1])   # 16 rows: the oracle's unit
+    idx = torch.from_numpy(sample).cuda()
+    xs = host(xd[idx].contiguous().view(torch.int16)).view(np.uint16)
+    ref = oracle_quant(xs, rht=True, rht_seed=W.RHT_SEED)
+    assert int(host(q.status)[0]) == 0
+    assert host(q.global_dec)[0].view(np.uint32) == np.float32(ref[2]).view(np.uint32)
+    assert np.array_equal(host(q.codes[idx]), ref[0])
+    assert np.array_equal(host(q.scales[idx]), ref[1])
+    del xd, q
+    torch.cuda.empty_cache()
+
+
 def test_sr_unbiased_64_seeds():
     """Workload 4 at 2048 x 5120: mean over 64 seeds of the stochastic codes equals the
     unrounded value (code units) -- z-test |mean z| <= 5 / sqrt(n)."""
