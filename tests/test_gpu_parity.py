@@ -542,6 +542,41 @@ def test_quantize_input_beyond_4gib():
     torch.cuda.empty_cache()
 
 
+def test_quantize_16x16_with_transpose_beyond_4gib():
+    # the weight path on a 4.3 GB input: 16x16 blocks with W^T from the same read.  The
+    # sampled tile rows (16 rows each, one holding the planted maximum) are quantized by the
+    # oracle alone; W and W^T must match it on those rows and on the matching columns of W^T.
+    say("quantize a 4.3 GB input with 16x16 blocks and W^T (65600 x 32768)")
+    rows, cols = 65600, 32768
+    g = torch.Generator(device="cuda").manual_seed(4)
+    xd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 8192):
+        r1 = min(rows, r0 + 8192)
+        xd[r0:r1] = (torch.randn((r1 - r0, cols), device="cuda", generator=g) * 0.2).clamp_(-1, 1).to(torch.bfloat16)
+    xd[40005, 777] = 100.0
+    q = N.quantize(xd, blocking="16x16", with_transpose=True)
+    torch.cuda.synchronize()
+    tile_rows = np.array([2500, 0, 2047, 4095, 4096, 4099])     # 2500 * 16 = 40000 holds the max
+    sample = (tile_rows[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+    idx = torch.from_numpy(sample).cuda()
+    xs = host(xd[idx].contiguous().view(torch.int16)).view(np.uint16)
+    ref = oracle_quant(xs, blocking="16x16")
+    assert host(q.global_dec)[0].view(np.uint32) == np.float32(ref[2]).view(np.uint32)
+    assert np.array_equal(host(q.codes[idx]), ref[0])
+    tidx = torch.from_numpy(tile_rows).cuda()
+    assert np.array_equal(host(q.scales[tidx]), ref[1])
+    # W^T: columns tr*16 .. tr*16+15 of W's sampled tile rows are bytes tr*8 .. tr*8+7
+    full = np.empty((len(sample), cols), np.uint8)
+    full[:, 0::2], full[:, 1::2] = ref[0] & 0xF, ref[0] >> 4
+    ft = np.ascontiguousarray(full.T)                            # cols x sampled rows
+    want = (ft[:, 0::2] | (ft[:, 1::2] << 4)).astype(np.uint8)   # cols x 8 * len(tile_rows)
+    bidx = torch.from_numpy((tile_rows[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)).cuda()
+    assert np.array_equal(host(q.codes_t[:, bidx]), want)
+    assert np.array_equal(host(q.scales_t[:, tidx]), np.ascontiguousarray(ref[1].T))
+    del xd, q
+    torch.cuda.empty_cache()
+
+
 def test_sr_unbiased_64_seeds():
     """Workload 4 at 2048 x 5120: mean over 64 seeds of the stochastic codes equals the
     unrounded value (code units) -- z-test |mean z| <= 5 / sqrt(n)."""
