@@ -577,6 +577,36 @@ def test_quantize_16x16_with_transpose_beyond_4gib():
     torch.cuda.empty_cache()
 
 
+def test_quantize_sr_beyond_4gib():
+    # stochastic rounding (two-pass) on a 4.3 GB input with the transform: the draws are
+    # indexed by the element's global position.  Every sampled 16-row block holds a planted
+    # 100 in an otherwise zero group (the tensor amax after the transform), so the oracle run
+    # on that block alone, with the block's Philox index base, sees the same tensor scale
+    # and the same draws.
+    say("quantize a 4.3 GB input with stochastic rounding (65600 x 32768, RHT, 1x16)")
+    rows, cols = 65600, 32768
+    g = torch.Generator(device="cuda").manual_seed(5)
+    xd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 8192):
+        r1 = min(rows, r0 + 8192)
+        xd[r0:r1] = (torch.randn((r1 - r0, cols), device="cuda", generator=g) * 0.2).clamp_(-1, 1).to(torch.bfloat16)
+    blocks = [0, 32768, 65520, rows - 16]
+    for b0 in blocks:   # the planted group is 100 and zeros: its transformed maximum is 25
+        xd[b0 + 3, 4096:4112] = 0.0   # exactly in every block (other groups stay <= 4)
+        xd[b0 + 3, 4101] = 100.0
+    kw = dict(rounding="sr", sr_seed=77, rht=True, rht_seed=W.RHT_SEED)
+    q = N.quantize(xd, **kw)
+    torch.cuda.synchronize()
+    for b0 in blocks:
+        xs = host(xd[b0:b0 + 16].contiguous().view(torch.int16)).view(np.uint16)
+        ref = oracle_quant(xs, sr_index_base=b0 * cols, **kw)
+        assert host(q.global_dec)[0].view(np.uint32) == np.float32(ref[2]).view(np.uint32)
+        assert np.array_equal(host(q.codes[b0:b0 + 16]), ref[0]), b0
+        assert np.array_equal(host(q.scales[b0:b0 + 16]), ref[1]), b0
+    del xd, q
+    torch.cuda.empty_cache()
+
+
 def test_sr_unbiased_64_seeds():
     """Workload 4 at 2048 x 5120: mean over 64 seeds of the stochastic codes equals the
     unrounded value (code units) -- z-test |mean z| <= 5 / sqrt(n)."""
