@@ -156,3 +156,35 @@ def test_autograd_function_matches_the_calls():
     for got, exact in ((y2, xf @ wf), (dx2, df @ wf.T), (dw2, xf.T @ df)):
         e = float((got.double() - exact).norm() / exact.norm())
         assert e < 0.25
+
+
+def test_dgrad_stochastic_rounding_is_unbiased():
+    # Why the recipe rounds gradients stochastically: averaged over seeds, dX = q(dY) W^T
+    # converges to dY W_q^T (the error of one draw shrinks ~1/sqrt(n)), while nearest-even
+    # rounding of dY leaves a fixed bias that no averaging removes.
+    say("Dgrad with SR: the mean over 32 seeds approaches dY W_q^T; RNE does not")
+    M, K, N_ = 256, 512, 384
+    x = to_dev(W.normal_scaled(M, K, seed=31, std=1.0))
+    w = to_dev(W.normal_scaled(K, N_, seed=32, std=0.05))
+    dy = to_dev(W.student_t(M, N_, seed=33))
+    _, ctx = L.linear_forward(x, w)
+    qw = ctx.qw
+    wq = torch.from_numpy(oracle.block_values_f64(host(qw.codes), host(qw.scales), K, N_, 1)
+                          * float(host(qw.global_dec)[0])).cuda()
+    target = dy.double() @ wq.T                     # the unquantized-gradient product
+    nrm = float(target.norm())
+    acc = torch.zeros_like(target)
+    single = None
+    for s in range(32):
+        qdy = N.quantize(dy, rounding="sr", sr_seed=s)
+        dx = N.gemm(qdy, qw, torch.float32).double()
+        acc += dx
+        if single is None:
+            single = float((dx - target).norm()) / nrm
+    mean_err = float((acc / 32 - target).norm()) / nrm
+    rne = N.gemm(N.quantize(dy), qw, torch.float32).double()
+    rne_err = float((rne - target).norm()) / nrm
+    say("  rel-fro vs dY W_q^T: one SR draw %.4f, mean of 32 SR draws %.4f, nearest-even %.4f"
+        % (single, mean_err, rne_err))
+    assert mean_err < single / 3
+    assert mean_err < rne_err / 2
