@@ -17,7 +17,8 @@ quantization could not carry a transform along K and along N at once.  Dgrad and
 draw their stochastic rounding with sr_seed and sr_seed + 1.
 
 This module only sequences library calls (quantize, transpose, GEMM); every arithmetic
-step runs in the HIP kernels.
+step runs in the HIP kernels.  M, K and N must be multiples of 16 (the quantizer's unit);
+a call that breaks this raises NVFP4Error from the first quantization.
 """
 from __future__ import annotations
 
