@@ -353,6 +353,20 @@ def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
         gomp.omp_set_num_threads(threads)
     except OSError:
         pass
+    # the GEMM alone on the dequantized operands: numpy binary64 and binary32 matmul (BLAS)
+    # on 1024 activation rows against the whole weight, in TFLOP/s
+    ca, sa, ga, _ = oracle.quantize(np.ascontiguousarray(x_np[:1024]), rht=True, rht_seed=W.RHT_SEED)
+    cwt, swt, gw, _ = oracle.quantize(np.ascontiguousarray(w_np.T), blocking=oracle.BLOCK_16x16)
+    a64 = oracle.block_values_f64(ca, sa, 1024, K, 0) * float(ga)
+    b64 = oracle.block_values_f64(cwt, swt, NN, K, 1) * float(gw)
+    fl = 2.0 * 1024 * NN * K
+    for name, dt in (("gemm_f64_TFLOPs", np.float64), ("gemm_f32_TFLOPs", np.float32)):
+        aa, bb = a64.astype(dt), np.ascontiguousarray(b64.T.astype(dt))
+        np.matmul(aa[:64], bb)
+        t0 = time.perf_counter()
+        np.matmul(aa, bb)
+        rates[name] = round(fl / (time.perf_counter() - t0) / 1e12, 4)
+    del a64, b64
     what = ("the whole step (all %d activation rows)" % M if sample_rows == M else
             "%d of %d activation rows, scaled to one step" % (sample_rows, M))
     return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
