@@ -583,24 +583,25 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
 }
 
 // ---------------------------------------------------------------- 16x16
-// A chunk is a block of up to kG16 tile-rows x 16 tile columns (128 x 256 elements); the
+// A chunk is a block of up to G tile-rows x 16 tile columns (G x 16 rows, 256 columns); the
 // 16 lanes of a DPP row hold the 16 rows of a tile, one tile-row per step, and the tile
 // amax is a DPP max over the row.  Codes of x are stored per step; with TRANS the codes
 // of x^T come from an in-register 4-bit transpose and are assembled in LDS, so that each
 // of the chunk's 256 rows of x^T is written as one segment of 8 bytes per tile-row.
+// G = 8 holds 64 MiB on chip (four workgroups per CU); a tensor that fits on chip in
+// chunks of G = 4 (five or six per CU) takes them: small tensors get twice the workgroups.
 constexpr int kT16 = 256;
 constexpr int kG16 = 8;
-constexpr int kTStride = kG16 * 8 + 8;   // LDS bytes per staged x^T row (+8 against bank conflicts)
-
-template <bool RHT, bool SR, bool TRANS>
+template <bool RHT, bool SR, bool TRANS, int G>
 __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t rk0,
     uint32_t rk1, uint32_t sk0, uint32_t sk1, uint64_t sr_base, uint32_t nchunks,
     uint64_t help, void *__restrict__ ws,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ codes_t,
     uint8_t *__restrict__ scales_t, float *__restrict__ global_dec, uint32_t *dev_status) {
-  __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTStride : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 16 * kG16 : 16];
+  constexpr int kTS = G * 8 + 8;   // LDS bytes per staged x^T row (+8 against bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTS : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 16 * G : 16];
   __shared__ float rtab[128];
   __shared__ uint32_t red[kT16 / 64];
   __shared__ uint32_t slot[2];
@@ -613,17 +614,17 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   const uint32_t cpr = (tpr + 15) >> 4;                // chunks per chunk-row
   const uint32_t tl = threadIdx.x >> 4, r = threadIdx.x & 15u;
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;   // transform along each lane's row group
-  uint4 ra[kG16], rb[kG16];
+  uint4 ra[G], rb[G];
 
   auto load_chunk = [&](uint32_t c) __attribute__((always_inline)) {
     const uint32_t br = c / cpr, bc = c - br * cpr;
-    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tr0 = br * G, nit = min((uint32_t)G, tpc - tr0);
     const uint32_t tc = bc * 16 + tl;
     const bool col_ok = tc < tpr;
     // a lane past the right edge loads the chunk's first tile (a valid address) and masks
     // the data, so the 16 lanes of a tile always run the reductions together
     const uint16_t *lane = x + ((int64_t)tr0 * 16 + r) * ld + (int64_t)(col_ok ? tc : bc * 16) * 16;
-    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+    static_for<0, G>([&](auto I) __attribute__((always_inline)) {
       constexpr int it = decltype(I)::value;
       const bool valid = col_ok && (uint32_t)it < nit;
       const uint4 *p = reinterpret_cast<const uint4 *>(lane + (int64_t)((uint32_t)it < nit ? it : 0) * 16 * ld);
@@ -634,11 +635,11 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   };
   auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold) __attribute__((always_inline)) {
     const uint32_t br = c / cpr, bc = c - br * cpr;
-    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tr0 = br * G, nit = min((uint32_t)G, tpc - tr0);
     const uint32_t tc = bc * 16 + tl;
     const bool col_ok = tc < tpr;
     if (TRANS) __syncthreads();   // the previous chunk's write-out has read the stage
-    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+    static_for<0, G>([&](auto I) __attribute__((always_inline)) {
       constexpr int it = decltype(I)::value;
       if ((uint32_t)it < nit) {   // uniform over the workgroup
         const uint32_t trw = tr0 + it;
@@ -663,8 +664,8 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         }
         if (TRANS) {
           transpose_nibbles16(q.x, q.y, r);   // lane r now holds column r of the tile
-          *reinterpret_cast<uint2 *>(tbuf + (tl * 16 + r) * kTStride + it * 8) = q;
-          if (r == 0) sbuf[tl * kG16 + it] = (uint8_t)sb;
+          *reinterpret_cast<uint2 *>(tbuf + (tl * 16 + r) * kTS + it * 8) = q;
+          if (r == 0) sbuf[tl * G + it] = (uint8_t)sb;
         }
       }
     });
@@ -672,20 +673,20 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
       __syncthreads();
       // 256 staged rows of x^T, nit * 8 bytes each: row j of the chunk is x^T row
       // bc*256 + j, bytes [tr0*8, tr0*8 + 8*nit)
-      for (uint32_t i = threadIdx.x; i < 256u * kG16; i += kT16) {
-        const uint32_t j = i / kG16, c8 = i % kG16;   // row, 8-byte piece
+      for (uint32_t i = threadIdx.x; i < 256u * G; i += kT16) {
+        const uint32_t j = i / G, c8 = i % G;   // row, 8-byte piece
         const uint32_t ttc = bc * 16 + (j >> 4);
         if (ttc < tpr && c8 < nit) {
-          const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTStride + c8 * 8);
+          const uint2 w = *reinterpret_cast<const uint2 *>(tbuf + j * kTS + c8 * 8);
           const int64_t trow = (int64_t)bc * 256 + j;
           *reinterpret_cast<uint2 *>(codes_t + trow * (rows >> 1) + (int64_t)tr0 * 8 + c8 * 8) = w;
         }
       }
       // scales of x^T: row ttc (one per tile column), bytes [tr0, tr0 + nit)
-      if (threadIdx.x < 16u * kG16) {
-        const uint32_t tcl = threadIdx.x / kG16, it = threadIdx.x % kG16;
+      if (threadIdx.x < 16u * G) {
+        const uint32_t tcl = threadIdx.x / G, it = threadIdx.x % G;
         const uint32_t ttc = bc * 16 + tcl;
-        if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + tr0 + it] = sbuf[tcl * kG16 + it];
+        if (ttc < tpr && it < nit) scales_t[(size_t)ttc * tpc + tr0 + it] = sbuf[tcl * G + it];
       }
     }
   };
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   // partial maximum of chunk c streamed from memory (for a chunk whose owner is late)
   auto partial = [&](uint32_t c) __attribute__((always_inline)) {
     const uint32_t br = c / cpr, bc = c - br * cpr;
-    const uint32_t tr0 = br * kG16, nit = min((uint32_t)kG16, tpc - tr0);
+    const uint32_t tr0 = br * G, nit = min((uint32_t)G, tpc - tr0);
     const uint32_t tc = bc * 16 + tl;
     uint32_t m = 0;
     if (tc < tpr) {
@@ -720,7 +721,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     load_chunk(c);
     uint32_t m = 0;
-    static_for<0, kG16>([&](auto I) __attribute__((always_inline)) {
+    static_for<0, G>([&](auto I) __attribute__((always_inline)) {
       constexpr int it = decltype(I)::value;
       m = max(m, lane_max(ra[it], rb[it]));
     });
@@ -753,16 +754,16 @@ uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Resident workgroups per CU of a kernel, times the CU count: the grid that gives every
 // resident slot one chunk.  A smaller number of resident workgroups is still correct.
-// Cached per device and kernel (the race on the cache is benign: every writer stores the
+// Cached per kernel and device (the race on the cache is benign: every writer stores the
 // same value).
-template <typename K>
-uint32_t resident_grid(K kernel, int threads) {
+template <auto Kern>
+uint32_t resident_grid(int threads) {
   static uint32_t cache[64] = {};
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(Kern),
                                                    threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const uint32_t g = (uint32_t)(cus * per_cu);
@@ -794,7 +795,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
 #define NVFP4_Q1(R, C)                                                                      \
   do {                                                                                      \
     auto k = quant_1x16_kernel<R, C>;                                                       \
-    uint32_t grid = resident_grid(k, kT1);                                                  \
+    uint32_t grid = resident_grid<quant_1x16_kernel<R, C>>(kT1);                            \
     if (grid > nchunks) grid = nchunks;                                                     \
     if (grid == 0) grid = 1;                                                                \
     k<<<grid, kT1, 0, stream>>>(q.x, ngroups, gpr, q.ld, q.cols, q.rht_k0, q.rht_k1,        \
@@ -830,18 +831,27 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
 #undef NVFP4_QSR
     return hipGetLastError();
   } else {
-    const uint32_t nchunks = (uint32_t)quantize_chunks(q.rows, q.cols, 1, q.rounding);
     const bool tr = q.codes_t != nullptr;
+    const uint64_t tile_rows = (uint64_t)(q.rows / 16), tile_cols = (uint64_t)(q.cols / 16);
+    const uint32_t n8 = (uint32_t)quantize_chunks(q.rows, q.cols, 1, q.rounding);
+    const uint64_t n4 = ceil_div(tile_rows, 4) * ceil_div(tile_cols, 16);
+    const bool small = kCoordBytes + 8 * n4 <= kWorkspaceBytes;
+#define NVFP4_Q16G(R, S, T, G, NCH)                                                         \
+  do {                                                                                      \
+    uint32_t grid = resident_grid<quant_16x16_kernel<R, S, T, G>>(kT16);                    \
+    if (grid > (NCH)) grid = (NCH);                                                         \
+    if (grid == 0) grid = 1;                                                                \
+    quant_16x16_kernel<R, S, T, G><<<grid, kT16, 0, stream>>>(                              \
+        q.x, q.rows, q.cols, q.ld, q.rht_k0, q.rht_k1, q.sr_k0, q.sr_k1, q.sr_base, (NCH),  \
+        help, q.ws, q.codes, q.scales, q.codes_t, q.scales_t, q.global_dec, q.dev_status);  \
+  } while (0)
+    // chunks of 4 tile-rows when the whole tensor then fits in the resident workgroups
 #define NVFP4_Q16(R, S, T)                                                                  \
   do {                                                                                      \
-    auto k = quant_16x16_kernel<R, S, T>;                                                   \
-    uint32_t grid = resident_grid(k, kT16);                                                 \
-    if (grid > nchunks) grid = nchunks;                                                     \
-    if (grid == 0) grid = 1;                                                                \
-    k<<<grid, kT16, 0, stream>>>(q.x, q.rows, q.cols, q.ld, q.rht_k0, q.rht_k1, q.sr_k0,    \
-                                 q.sr_k1, q.sr_base, nchunks, help, q.ws, q.codes,          \
-                                 q.scales, q.codes_t, q.scales_t, q.global_dec,             \
-                                 q.dev_status);                                             \
+    if (small && n4 <= resident_grid<quant_16x16_kernel<R, S, T, 4>>(kT16))                 \
+      NVFP4_Q16G(R, S, T, 4, (uint32_t)n4);                                                 \
+    else                                                                                    \
+      NVFP4_Q16G(R, S, T, kG16, n8);                                                        \
   } while (0)
     if (rht) {
       if (sr) { if (tr) NVFP4_Q16(true, true, true); else NVFP4_Q16(true, true, false); }
@@ -851,6 +861,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
       else { if (tr) NVFP4_Q16(false, false, true); else NVFP4_Q16(false, false, false); }
     }
 #undef NVFP4_Q16
+#undef NVFP4_Q16G
   }
   return hipGetLastError();
 }
