@@ -110,9 +110,9 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
   return from_hip(nvfp4::launch_dequantize(d, reinterpret_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
-                        int64_t K, void *c, int64_t ldc, int32_t out_dtype,
-                        nvfp4_stream_t stream) {
+static nvfp4_status gemm_call(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
+                              int64_t K, void *c, int64_t ldc, int32_t out_dtype, void *ws,
+                              nvfp4_stream_t stream) {
   if (!a || !b) return NVFP4_ERR_NULL;
   if (!mult16(M) || !mult16(N) || !mult16(K) || ldc < N || M > (1 << 30) || N > (1 << 30) ||
       K > (1 << 23) || too_many_tiles(M, N))
@@ -139,7 +139,24 @@ nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t 
   g.ldc = ldc;
   g.out_f32 = out_dtype == NVFP4_OUT_FP32;
   g.c = c;
+  g.ws = ws;
   return from_hip(nvfp4::launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
+                        int64_t K, void *c, int64_t ldc, int32_t out_dtype,
+                        nvfp4_stream_t stream) {
+  return gemm_call(a, b, M, N, K, c, ldc, out_dtype, nullptr, stream);
+}
+
+size_t nvfp4_gemm_workspace_bytes(void) { return nvfp4::kGemmWorkspaceBytes; }
+
+nvfp4_status nvfp4_gemm_ws(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
+                           int64_t K, void *c, int64_t ldc, int32_t out_dtype, void *workspace,
+                           size_t workspace_bytes, nvfp4_stream_t stream) {
+  if (!workspace || workspace_bytes < nvfp4::kGemmWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+  return gemm_call(a, b, M, N, K, c, ldc, out_dtype, workspace, stream);
 }
 
 nvfp4_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,

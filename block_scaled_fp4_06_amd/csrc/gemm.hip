@@ -219,16 +219,32 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t w, int h) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * h), 1.0f, false);
 }
 
+// Work items.  Workgroups 0 .. t_dp-1 each compute one whole tile (t_dp is all tiles, or
+// the tiles of the full rounds when the last round would leave CUs idle).  With a
+// workspace, each remaining tile is split along K into `splits` contiguous ranges of K
+// steps, one workgroup each: every split item stores its fp32 partial tile in the
+// workspace and counts itself on the tile's counter; the last to arrive sums the
+// partials in split order (so the result does not depend on arrival order), resets the
+// counter and runs the epilogue.  No workgroup waits for another.
 template <bool F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
+void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits, uint8_t *ws) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageB2];
+  __shared__ uint32_t sk_last;
 
   // tile order: the workgroups that one XCD (block id % 8) runs form a contiguous
   // range of tiles, walked four tile-rows at a time so concurrent tiles share A and B
-  const int G = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int nk_all = p.K / 256;
+  int b = blockIdx.x, item = -1, kbeg = 0, kend = nk_all;
+  if (b < t_dp) {
+    if ((t_dp & 7) == 0) b = (b & 7) * (t_dp >> 3) + (b >> 3);
+  } else {
+    item = b - t_dp;
+    const int sp = item % splits;
+    b = t_dp + item / splits;
+    kbeg = (int)((int64_t)sp * nk_all / splits);
+    kend = (int)((int64_t)(sp + 1) * nk_all / splits);
+  }
   const int gm = 4;
   const int band = b / (gm * tiles_n), in_band = b - band * gm * tiles_n;
   const int rows_in_band = min(gm, tiles_m - band * gm);
@@ -241,7 +257,7 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t rowb = p.K >> 1;
   const int kgroups = p.K >> 4;
-  const int nk = p.K / 256;
+  const int nk = kend - kbeg;   // K steps of this work item, from step kbeg
 
   // Tiles travel through registers: bounds-checked 16-byte buffer loads (a row past the
   // end of an operand reads zeros, and zero codes and scales contribute nothing; those
@@ -270,15 +286,15 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
   auto gload_part = [&](int kb, int q) {
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + kb * kRowB2));
+      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + (kbeg + kb) * kRowB2));
       sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_code, soff, 0);
       stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff_code, soff, 0);
     }
     if (q == 3) {
       ssa = __builtin_amdgcn_raw_buffer_load_b128(
-          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane((uint32_t)(kb * 16)), 0);
+          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane((uint32_t)((kbeg + kb) * 16)), 0);
       ssb = __builtin_amdgcn_raw_buffer_load_b128(
-          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane((uint32_t)(kb * 16)), 0);
+          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane((uint32_t)((kbeg + kb) * 16)), 0);
     }
   };
   auto gload = [&](int kb) {
@@ -395,6 +411,56 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }
   }
 
+  if (item >= 0) {
+    // Split item: the partial tile goes to its slot as [wave][i][jj][r / 2][lane] pairs,
+    // then the item counts itself.  Slots are written and read with agent-scope (relaxed
+    // atomic) accesses, which are coherent across the XCDs' L2 caches by themselves, and
+    // the count is taken only after every store of the workgroup has completed: no cache
+    // write-back or invalidation is needed, which would also flush the L2 under the other
+    // workgroups of the XCD.  The last arrival sums all slots of the tile in split order.
+    uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kGemmCtrBytes);
+    const int tile = item / splits;
+    constexpr int kSlot = kT2 * kT2 / 2;   // pairs per slot
+    uint64_t *mine = slots + (size_t)item * kSlot + wave * (kSlot / 4) + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint64_t v = (uint64_t)__float_as_uint(acc[i][jj][2 * q]) |
+                             ((uint64_t)__float_as_uint(acc[i][jj][2 * q + 1]) << 32);
+          __hip_atomic_store(mine + ((i * 4 + jj) * 8 + q) * 64, v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t *ctr = reinterpret_cast<uint32_t *>(ws) + tile;
+      const uint32_t before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = before == (uint32_t)splits - 1u;
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sk_last = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!sk_last) return;
+    const uint64_t *first = slots + (size_t)tile * splits * kSlot + wave * (kSlot / 4) + lane;
+    for (int sp = 0; sp < splits; ++sp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint64_t v = __hip_atomic_load(first + (size_t)sp * kSlot + ((i * 4 + jj) * 8 + q) * 64,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float lo = __uint_as_float((uint32_t)v), hi = __uint_as_float((uint32_t)(v >> 32));
+            acc[i][jj][2 * q] = sp == 0 ? lo : acc[i][jj][2 * q] + lo;
+            acc[i][jj][2 * q + 1] = sp == 0 ? hi : acc[i][jj][2 * q + 1] + hi;
+          }
+    }
+  }
+
   // Epilogue.  Accumulator element r of block (i, jj) sits at row 32 i + 8 (r / 4) + 4 h +
   // r % 4 and column 32 jj + l32 of the wave's 128 x 128 block.  A tile wholly inside C
   // takes the unchecked path: one row address per (i, r), the four column blocks as
@@ -445,6 +511,21 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n) {
       }
 }
 
+constexpr int kMinSplitSteps = 16;
+
+// Compute units of the current device (cached per device; a racing writer stores the
+// same value).
+int cu_count() {
+  static int cache[64] = {};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  return cus;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
@@ -455,8 +536,27 @@ hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
   p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K; p.ldc = g.ldc; p.c = g.c;
   if (g.K > 0 && g.K % 256 == 0) {
     const int tm = (int)((g.M + kT2 - 1) / kT2), tn = (int)((g.N + kT2 - 1) / kT2);
-    if (g.out_f32) gemm256_kernel<true><<<tm * tn, 256, 0, stream>>>(p, tm, tn);
-    else gemm256_kernel<false><<<tm * tn, 256, 0, stream>>>(p, tm, tn);
+    const int tiles = tm * tn, nk = (int)(g.K / 256);
+    // One workgroup per CU: split the tiles of a last, partial round along K so that it
+    // keeps every CU busy.  A split item moves 256 KB of partial tile out and its tile's
+    // last item moves all of them back in, about the time of a few K steps, so each item
+    // keeps at least kMinSplitSteps K steps (at most 8 splits).
+    int t_dp = tiles, splits = 1;
+    if (g.ws) {
+      const int cus = cu_count();
+      const int rest = tiles % cus;
+      if (rest > 0) {
+        int sp = min(min(cus, kGemmMaxItems) / rest, min(8, nk / kMinSplitSteps));
+        if (sp >= 2) {
+          t_dp = tiles - rest;
+          splits = sp;
+        }
+      }
+    }
+    const unsigned grid = (unsigned)(t_dp + (tiles - t_dp) * splits);
+    uint8_t *ws = static_cast<uint8_t *>(g.ws);
+    if (g.out_f32) gemm256_kernel<true><<<grid, 256, 0, stream>>>(p, tm, tn, t_dp, splits, ws);
+    else gemm256_kernel<false><<<grid, 256, 0, stream>>>(p, tm, tn, t_dp, splits, ws);
     return hipGetLastError();
   }
   const int tiles_n = (int)((g.N + kBN - 1) / kBN);

@@ -55,7 +55,14 @@ struct GemmLaunch {
   int64_t M, N, K, ldc;
   int out_f32;
   void *c;
+  void *ws = nullptr;   // optional: lets the last, partial round of tiles split along K
 };
+
+// GEMM workspace: one arrival counter per split tile, then the fp32 partial tiles (256 x
+// 256) of at most kGemmMaxItems split work items.
+constexpr size_t kGemmCtrBytes = 4096;
+constexpr int kGemmMaxItems = 256;
+constexpr size_t kGemmWorkspaceBytes = kGemmCtrBytes + (size_t)kGemmMaxItems * 256 * 256 * 4;
 
 hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream);
 

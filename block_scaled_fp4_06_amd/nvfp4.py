@@ -46,7 +46,7 @@ class NVFP4Error(RuntimeError):
 
 
 EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
-            "nvfp4_gemm", "nvfp4_transpose_bf16", "mxfp4_quantize", "mxfp4_dequantize",
+            "nvfp4_gemm", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_transpose_bf16", "mxfp4_quantize", "mxfp4_dequantize",
             "mxfp4_gemm",
             "nvfp4_status_string", "nvfp4_abi_version")
 
@@ -73,6 +73,11 @@ def load(path: str = LIB_PATH):
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
                              P, i64, i32, P]
     L.nvfp4_gemm.restype = ctypes.c_int
+    L.nvfp4_gemm_workspace_bytes.argtypes = []
+    L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.nvfp4_gemm_ws.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
+                                P, i64, i32, P, ctypes.c_size_t, P]
+    L.nvfp4_gemm_ws.restype = ctypes.c_int
     L.nvfp4_transpose_bf16.argtypes = [P, i64, i64, i64, P, i64, P]
     L.nvfp4_transpose_bf16.restype = ctypes.c_int
     L.mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P]
@@ -110,6 +115,16 @@ def nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y, ld_y, o
 def nvfp4_gemm(a: Operand, b: Operand, M, N, K, c, ldc, out_dtype, stream) -> int:
     return int(load().nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, c, ldc,
                                  out_dtype, stream))
+
+
+def nvfp4_gemm_workspace_bytes() -> int:
+    return int(load().nvfp4_gemm_workspace_bytes())
+
+
+def nvfp4_gemm_ws(a: Operand, b: Operand, M, N, K, c, ldc, out_dtype, ws, ws_bytes,
+                  stream) -> int:
+    return int(load().nvfp4_gemm_ws(ctypes.byref(a), ctypes.byref(b), M, N, K, c, ldc,
+                                    out_dtype, ws, ws_bytes, stream))
 
 
 def nvfp4_transpose_bf16(x, rows, cols, ld_x, y, ld_y, stream) -> int:
@@ -241,21 +256,49 @@ def dequantize(q: NVFP4Tensor, out_dtype=None, stream=None, out=None):
     return out
 
 
-def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None):
-    """C = A . B^T with A (M x K) and B (N x K) NVFP4 operands."""
+_GEMM_WORKSPACES = {}
+
+
+def new_gemm_workspace(device):
+    """A GEMM workspace: nvfp4_gemm_workspace_bytes() bytes, zero-filled as the library
+    requires before first use."""
+    import torch
+    return torch.zeros(nvfp4_gemm_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None,
+         workspace=None, split_tail=True):
+    """C = A . B^T with A (M x K) and B (N x K) NVFP4 operands.
+
+    split_tail: run nvfp4_gemm_ws, which splits the tiles of a last, partial round along K
+    (workspace: optional tensor from new_gemm_workspace(), used by one stream at a time; by
+    default one cached workspace per (device, stream)); False runs nvfp4_gemm."""
     import torch
     if a.cols != b.cols:
         raise ValueError("K mismatch: %d vs %d" % (a.cols, b.cols))
     out_dtype = out_dtype or torch.bfloat16
+    dev = a.codes.device
     if out is None:
-        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=dev)
     od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     oa = Operand(a.codes.data_ptr(), a.scales.data_ptr(), a.global_dec.data_ptr(), a.blocking, 0)
     ob = Operand(b.codes.data_ptr(), b.scales.data_ptr(), b.global_dec.data_ptr(), b.blocking, 0)
-    rc = nvfp4_gemm(oa, ob, a.rows, b.rows, a.cols, _ptr(out), out.stride(0), od,
-                    _stream(stream, a.codes.device))
+    sh = _stream(stream, dev)
+    if split_tail:
+        ws = workspace
+        if ws is None:
+            key = (dev.index, sh.value)
+            ws = _GEMM_WORKSPACES.get(key)
+            if ws is None:
+                ws = _GEMM_WORKSPACES[key] = new_gemm_workspace(dev)
+        rc = nvfp4_gemm_ws(oa, ob, a.rows, b.rows, a.cols, _ptr(out), out.stride(0), od,
+                           _ptr(ws), ws.numel(), sh)
+        name = "nvfp4_gemm_ws"
+    else:
+        rc = nvfp4_gemm(oa, ob, a.rows, b.rows, a.cols, _ptr(out), out.stride(0), od, sh)
+        name = "nvfp4_gemm"
     if rc != NVFP4_OK:
-        raise NVFP4Error(rc, "nvfp4_gemm")
+        raise NVFP4Error(rc, name)
     return out
 
 

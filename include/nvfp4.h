@@ -56,7 +56,7 @@ typedef enum {
     NVFP4_ERR_SHAPE = 2,       /* a size is negative or not a multiple of 16, or ld too small */
     NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned or ld not a multiple of 8 */
     NVFP4_ERR_UNSUPPORTED = 4, /* an option combination this version does not implement */
-    NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than nvfp4_quantize_workspace_bytes */
+    NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the *_workspace_bytes value */
     NVFP4_ERR_HIP = 6          /* a HIP launch failed */
 } nvfp4_status;
 
@@ -163,6 +163,28 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
 nvfp4_status nvfp4_gemm(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
                         int64_t K, void *c, int64_t ldc, int32_t out_dtype,
                         nvfp4_stream_t stream);
+
+/* Bytes of device memory nvfp4_gemm_ws needs as its workspace (caller-allocated; the same
+ * value for every shape): 4 KiB of counters and 256 fp32 partial tiles of 256 x 256. */
+size_t nvfp4_gemm_workspace_bytes(void);
+
+/*
+ * nvfp4_gemm_ws -- the product of nvfp4_gemm ([NV-blog] recipe section, Figure 1
+ * paragraph), with a workspace.  The GEMM runs one 256 x 256 tile per compute unit at a
+ * time; when the tile count is not a multiple of the compute units, the tiles of the last
+ * round are split along K over otherwise idle units, their fp32 partial tiles summed in
+ * the workspace in a fixed order (the result does not depend on scheduling, but may differ
+ * from nvfp4_gemm's in the last bits: the K sum is associated differently).
+ * Arguments as nvfp4_gemm, and:
+ * workspace        (device) at least nvfp4_gemm_workspace_bytes() bytes, 16-byte aligned,
+ *                  zero-filled before its first use; every call leaves its counters at zero
+ *                  again.  A workspace serves one stream: calls that use it must not overlap.
+ * workspace_bytes  its size.
+ * Errors: as nvfp4_gemm; NVFP4_ERR_WORKSPACE for a NULL or short workspace.
+ */
+nvfp4_status nvfp4_gemm_ws(const nvfp4_operand *a, const nvfp4_operand *b, int64_t M, int64_t N,
+                           int64_t K, void *c, int64_t ldc, int32_t out_dtype, void *workspace,
+                           size_t workspace_bytes, nvfp4_stream_t stream);
 
 /*
  * nvfp4_transpose_bf16 -- y = x^T for a bf16 tensor (bit patterns are moved, not changed).

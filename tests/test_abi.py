@@ -130,6 +130,27 @@ def test_gemm_argument_errors(lib):
     assert gm(M=0, a=op(codes=None, scales=None, g=None), c=None) == ERR["OK"]
 
 
+def test_gemm_ws_argument_errors(lib):
+    wsb = N.nvfp4_gemm_workspace_bytes()
+    # counters plus 256 partial tiles of 256 x 256 fp32
+    assert wsb == 4096 + 256 * 256 * 256 * 4
+
+    def op(codes=FAKE, scales=FAKE, g=FAKE, blk=0):
+        return N.Operand(codes, scales, g, blk, 0)
+
+    def gm(ws=FAKE, nbytes=wsb, M=32, K=64, c=FAKE, ldc=32, a=None):
+        return N.nvfp4_gemm_ws(a or op(), op(blk=1), M, 32, K, c, ldc, 0, ws, nbytes, None)
+    assert gm(ws=None) == ERR["WORKSPACE"]
+    assert gm(nbytes=wsb - 1) == ERR["WORKSPACE"]
+    assert gm(ws=FAKE + 8) == ERR["ALIGN"]
+    # then the checks of nvfp4_gemm
+    assert gm(K=40) == ERR["SHAPE"]
+    assert gm(c=None) == ERR["NULL"]
+    assert gm(ldc=36) == ERR["ALIGN"]
+    assert gm(a=op(codes=None)) == ERR["NULL"]
+    assert gm(M=0, c=None) == ERR["OK"]
+
+
 def test_mx_argument_errors(lib):
     def q(x=FAKE, rows=32, cols=64, ld=64, codes=FAKE, scales=FAKE):
         return N.mxfp4_quantize(x, rows, cols, ld, codes, scales, None)

@@ -480,6 +480,99 @@ def test_gemm_w5_full_sampled():
     gemm_check(qa, qw.transposed(), ref_a, ref_b, 8192, 20480, 5120, rows=rows)
 
 
+def spread_blocks(x_bits, seed, octaves=12):
+    """bf16 input whose 16-element row groups are scaled by 2^-j, j uniform in 0..octaves:
+    block scales then span ~2^12, so fp32 sums of the products round."""
+    rng = np.random.default_rng(seed)
+    f = W.bf16_bits_to_f32(x_bits).reshape(x_bits.shape[0], -1, 16)
+    f = f * np.exp2(-rng.integers(0, octaves + 1, size=f.shape[:2] + (1,))).astype(np.float32)
+    return W.f32_to_bf16_bits(f.reshape(x_bits.shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N_,K,spread", [(4096, 5120, 8192, False), (528, 800, 8192, False),
+                                           (256, 256, 32768, False), (528, 800, 8192, True),
+                                           (256, 256, 32768, True)])
+def test_gemm_split_tail(M, N_, K, spread):
+    # nvfp4_gemm_ws splits the tiles of the last, partial round along K, each split keeping
+    # at least 16 K steps (4096 x 5120: 256 whole tiles, then 64 tiles in 2 K ranges;
+    # 528 x 800: 12 edge-heavy tiles in 2; 256 x 256: one tile in 8): against the oracle
+    # on rows of both kinds of tiles, against the unsplit kernel, bit-identical from run to
+    # run, counters back at zero.  On the plain workloads every fp32 partial sum is exact
+    # (the products sit on a coarse grid: block scales within a few octaves), so split and
+    # unsplit agree bit for bit; with block magnitudes spread over 12 octaves the sums
+    # round and the two differ within the fp32 summation bound.
+    say("gemm split tail %dx%dx%d%s" % (M, N_, K, " (spread blocks)" if spread else ""))
+    a = W.channel_outliers(M, K, seed=M + 3)
+    if spread:
+        a = spread_blocks(a, seed=M)
+    w = W.normal_scaled(K, N_, seed=N_ + 4, std=0.02)
+    ka = dict(rht=True, rht_seed=W.RHT_SEED)
+    qa, ref_a = run_quant(a, **ka), oracle_quant(a, **ka)
+    qw = run_quant(w, blocking="16x16", with_transpose=True)
+    qb = qw.transposed()
+    ref_b = oracle_quant(np.ascontiguousarray(w.T), blocking="16x16")
+    assert np.array_equal(host(qb.codes), ref_b[0])
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), [0, M - 1],
+                                     rng.choice(np.arange(M - M // 4, M), 16, replace=False)]))
+    gemm_check(qa, qb, ref_a, ref_b, M, N_, K, rows=rows)
+    ws = N.new_gemm_workspace(qa.codes.device)
+    c1 = N.gemm(qa, qb, torch.float32, workspace=ws)
+    c2 = N.gemm(qa, qb, torch.float32, workspace=ws)
+    c0 = N.gemm(qa, qb, torch.float32, split_tail=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert int(ws[:4096].count_nonzero()) == 0
+    assert int(ws[4096:].count_nonzero()) > 0       # the split path ran: partial tiles
+    d = float((c1.double() - c0.double()).norm() / c0.double().norm())
+    say("  split vs unsplit: rel-fro %.3g, %d elements differ" % (d, int((c1 != c0).sum())))
+    assert d <= 1e-5
+    qa64 = oracle.block_values_f64(ref_a[0], ref_a[1], M, K, 0)[rows] * float(ref_a[2])
+    qb64 = oracle.block_values_f64(ref_b[0], ref_b[1], N_, K, 1) * float(ref_b[2])
+    u = 2.0 ** -24
+    bound = 2 * (K * u / (1 - K * u) + 3 * u) * (np.abs(qa64) @ np.abs(qb64).T) + 1e-37
+    diff = np.abs(host(c1)[rows].astype(np.float64) - host(c0)[rows].astype(np.float64))
+    assert np.all(diff <= bound)
+
+
+def test_gemm_split_tail_graph_replay():
+    # counters reset by the last arrival of every launch: a captured split GEMM replayed on
+    # changing operands, with eager calls on the same workspace in between
+    say("HIP graph replay of a split GEMM (12 tiles x 2 K ranges) on changing inputs")
+    M, N_, K = 528, 800, 8192
+    ka = dict(rht=True, rht_seed=W.RHT_SEED)
+    ins = []
+    for sd in (31, 32, 33):
+        a = W.channel_outliers(M, K, seed=sd)
+        w = W.normal_scaled(K, N_, seed=sd + 10, std=0.02)
+        ins.append((run_quant(a, **ka), run_quant(w, blocking="16x16", with_transpose=True).transposed()))
+    qa, qb = run_quant(W.channel_outliers(M, K, seed=30), **ka), ins[0][1]
+    qb = N.NVFP4Tensor(qb.codes.clone(), qb.scales.clone(), qb.global_dec.clone(), qb.rows,
+                       qb.cols, qb.blocking)
+    ws = N.new_gemm_workspace(qa.codes.device)
+    out = torch.empty((M, N_), dtype=torch.float32, device=qa.codes.device)
+    N.gemm(qa, qb, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        N.gemm(qa, qb, out=out, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    for i in (1, 0, 2, 2, 1):
+        xa, xb = ins[i]
+        for dst, src in ((qa.codes, xa.codes), (qa.scales, xa.scales), (qa.global_dec, xa.global_dec),
+                         (qb.codes, xb.codes), (qb.scales, xb.scales), (qb.global_dec, xb.global_dec)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = N.gemm(xa, xb, torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        assert int(ws[:4096].count_nonzero()) == 0
+
+
 def test_gemm_operand_beyond_2gib():
     # A of 524800 x 8192 (2.15 GB of codes): rows past the 2^31-byte mark must be read,
     # not returned as zero by a clamped buffer range.  Codes and E4M3 scales are drawn
