@@ -353,6 +353,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   constexpr bool SR = false;   // stochastic rounding takes the two-pass kernels below
   uint4 ra[kG1], rb[kG1];
+  uint32_t gm[kG1];   // row-group maxima of the chunk held in registers, from phase 1
 
   auto load_chunk = [&](uint32_t c) __attribute__((always_inline)) {
     const uint32_t base = c * kChunk1;
@@ -388,7 +389,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     return wg_max<kT1>(m, red);
   };
-  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold) __attribute__((always_inline)) {
+  // HAVE_MAX: the chunk phase 1 left in registers, whose group maxima gm[] it kept (the
+  // same bits as the maximum of the transformed values here: see rht16_absmax_bits)
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold, auto have_max) __attribute__((always_inline)) {
+    constexpr bool HAVE_MAX = decltype(have_max)::value != 0;
     const uint32_t base = c * kChunk1;
     static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
@@ -397,7 +401,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         float v[16];
         unpack16(ra[i], rb[i], v);
         if (RHT) rht16_unscaled(v, sm);           // v = 4 y
-        const float bmax = RHT ? absmax16(v) * 0.25f : absmax16(v);
+        const float amax = HAVE_MAX ? __uint_as_float(gm[i]) : absmax16(v);
+        const float bmax = RHT ? amax * 0.25f : amax;
         const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
         const float rr = rtab[sb];
         if (RHT && !fold) {
@@ -422,7 +427,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     uint32_t m = 0;
     static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
-      m = max(m, group_max(ra[i], rb[i]));
+      gm[i] = group_max(ra[i], rb[i]);
+      m = max(m, gm[i]);
     });
     m = wg_max<kT1>(m, red);
     if (tid == 0) store_relaxed(words + c, tagged(tok, m));
@@ -442,10 +448,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   if (ts.finite && !failed) {
     const bool fold = build_rtab(rtab, ts.enc, RHT);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
-      encode_chunk(last, ts, fold);
+      encode_chunk(last, ts, fold, Idx<1>{});
       for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
         load_chunk(c);
-        encode_chunk(c, ts, fold);
+        encode_chunk(c, ts, fold, Idx<0>{});
       }
     }
   }
