@@ -210,7 +210,7 @@ __device__ __forceinline__ uint32_t wg_amax(uint64_t *gword, uint64_t *words, ui
     const uint64_t t0 = (uint64_t)wall_clock64();
     uint64_t g = load_relaxed(gword);
     while (!has_tag(g, tok) && (uint64_t)wall_clock64() - t0 < help) {
-      __builtin_amdgcn_s_sleep(16);
+      __builtin_amdgcn_s_sleep(2);
       g = load_relaxed(gword);
     }
     slot[0] = has_tag(g, tok) ? 1u : 0u;
