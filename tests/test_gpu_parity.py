@@ -535,6 +535,23 @@ def test_gemm_split_tail(M, N_, K, spread):
     assert np.all(diff <= bound)
 
 
+def test_gemm_split_tail_strided_output():
+    # the last split item writes through the same epilogue: a row stride wider than N
+    # (both output types), padding columns untouched
+    say("gemm split tail into a strided C (ldc 832 > N 800)")
+    M, N_, K = 528, 800, 8192
+    qa = run_quant(W.channel_outliers(M, K, seed=41), rht=True, rht_seed=W.RHT_SEED)
+    qb = run_quant(W.normal_scaled(K, N_, seed=42, std=0.02), blocking="16x16",
+                   with_transpose=True).transposed()
+    for dt in (torch.float32, torch.bfloat16):
+        ref = N.gemm(qa, qb, dt)
+        big = torch.zeros((M, 832), dtype=dt, device=ref.device)
+        N.gemm(qa, qb, out=big[:, :N_])
+        torch.cuda.synchronize()
+        assert torch.equal(big[:, :N_], ref)
+        assert int(big[:, N_:].count_nonzero()) == 0
+
+
 def test_gemm_split_tail_graph_replay():
     # counters reset by the last arrival of every launch: a captured split GEMM replayed on
     # changing operands, with eager calls on the same workspace in between
