@@ -412,26 +412,28 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
   }
 
   if (item >= 0) {
-    // Split item: the partial tile goes to its slot as [wave][i][jj][r / 2][lane] pairs,
-    // then the item counts itself.  Slots are written and read with agent-scope (relaxed
-    // atomic) accesses, which are coherent across the XCDs' L2 caches by themselves, and
-    // the count is taken only after every store of the workgroup has completed: no cache
-    // write-back or invalidation is needed, which would also flush the L2 under the other
-    // workgroups of the XCD.  The last arrival sums all slots of the tile in split order.
-    uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kGemmCtrBytes);
+    // Split item: the partial tile goes to its slot as [wave][i][jj][r / 4][lane] groups of
+    // four, then the item counts itself.  Slots are written and read by 128-bit buffer
+    // accesses with the agent-scope cache policy (aux 16: the bits the compiler gives
+    // agent-scope atomic loads and stores), which are coherent across the XCDs' L2 caches
+    // by themselves, and the count is taken only after every store of the workgroup has
+    // completed: no cache write-back or invalidation is needed, which would also flush the
+    // L2 under the other workgroups of the XCD.  The last arrival sums all slots of the
+    // tile in split order.
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ws + kGemmCtrBytes, (int64_t)kGemmMaxItems * kT2 * kT2 * 4);
     const int tile = item / splits;
-    constexpr int kSlot = kT2 * kT2 / 2;   // pairs per slot
-    uint64_t *mine = slots + (size_t)item * kSlot + wave * (kSlot / 4) + lane;
+    constexpr int kSlotB = kT2 * kT2 * 4;   // bytes per slot
+    const int lane_off = (wave * 16 * 4 * 64 + lane) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint64_t v = (uint64_t)__float_as_uint(acc[i][jj][2 * q]) |
-                             ((uint64_t)__float_as_uint(acc[i][jj][2 * q + 1]) << 32);
-          __hip_atomic_store(mine + ((i * 4 + jj) * 8 + q) * 64, v, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < 4; ++q) {
+          v4i32 v = {(int)__float_as_uint(acc[i][jj][4 * q]), (int)__float_as_uint(acc[i][jj][4 * q + 1]),
+                     (int)__float_as_uint(acc[i][jj][4 * q + 2]), (int)__float_as_uint(acc[i][jj][4 * q + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, lane_off + ((i * 4 + jj) * 4 + q) * 64 * 16,
+                                                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(item * kSlotB)), 16);
         }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
     __syncthreads();
@@ -444,19 +446,20 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
     }
     __syncthreads();
     if (!sk_last) return;
-    const uint64_t *first = slots + (size_t)tile * splits * kSlot + wave * (kSlot / 4) + lane;
     for (int sp = 0; sp < splits; ++sp) {
+      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)((tile * splits + sp) * kSlotB));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint64_t v = __hip_atomic_load(first + (size_t)sp * kSlot + ((i * 4 + jj) * 8 + q) * 64,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float lo = __uint_as_float((uint32_t)v), hi = __uint_as_float((uint32_t)(v >> 32));
-            acc[i][jj][2 * q] = sp == 0 ? lo : acc[i][jj][2 * q] + lo;
-            acc[i][jj][2 * q + 1] = sp == 0 ? hi : acc[i][jj][2 * q + 1] + hi;
+          for (int q = 0; q < 4; ++q) {
+            const v4i32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + ((i * 4 + jj) * 4 + q) * 64 * 16, soff, 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = __uint_as_float((uint32_t)v[e]);
+              acc[i][jj][4 * q + e] = sp == 0 ? f : acc[i][jj][4 * q + e] + f;
+            }
           }
     }
   }
@@ -511,7 +514,7 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
       }
 }
 
-constexpr int kMinSplitSteps = 16;
+constexpr int kMinSplitSteps = 8;
 
 // Compute units of the current device (cached per device; a racing writer stores the
 // same value).

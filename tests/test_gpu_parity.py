@@ -494,8 +494,8 @@ def spread_blocks(x_bits, seed, octaves=12):
                                            (256, 256, 32768, True)])
 def test_gemm_split_tail(M, N_, K, spread):
     # nvfp4_gemm_ws splits the tiles of the last, partial round along K, each split keeping
-    # at least 16 K steps (4096 x 5120: 256 whole tiles, then 64 tiles in 2 K ranges;
-    # 528 x 800: 12 edge-heavy tiles in 2; 256 x 256: one tile in 8): against the oracle
+    # at least 8 K steps (4096 x 5120: 256 whole tiles, then 64 tiles in 4 K ranges;
+    # 528 x 800: 12 edge-heavy tiles in 4; 256 x 256: one tile in 8): against the oracle
     # on rows of both kinds of tiles, against the unsplit kernel, bit-identical from run to
     # run, counters back at zero.  On the plain workloads every fp32 partial sum is exact
     # (the products sit on a coarse grid: block scales within a few octaves), so split and
@@ -555,7 +555,7 @@ def test_gemm_split_tail_strided_output():
 def test_gemm_split_tail_graph_replay():
     # counters reset by the last arrival of every launch: a captured split GEMM replayed on
     # changing operands, with eager calls on the same workspace in between
-    say("HIP graph replay of a split GEMM (12 tiles x 2 K ranges) on changing inputs")
+    say("HIP graph replay of a split GEMM (12 tiles x 4 K ranges) on changing inputs")
     M, N_, K = 528, 800, 8192
     ka = dict(rht=True, rht_seed=W.RHT_SEED)
     ins = []
