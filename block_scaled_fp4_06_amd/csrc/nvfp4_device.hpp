@@ -122,28 +122,20 @@ __device__ __forceinline__ uint32_t e2m1_rn_mag(float a) {
 }
 
 // Stochastic magnitude code of a >= 0 with the 16-bit random integer k: round up iff
-// (k + 1/2) / 2^16 < (a - lo) / (hi - lo), evaluated as 2k + 1 < (a - lo) * 2^17 / step.
-// Every quantity is exact in binary32 (a - lo is exact, the step and 2^17 are powers of
-// two, 2k + 1 < 2^17), so both forms decide alike.  Below 1 the grid step is 1/2 (codes
-// 0, 1, 2); from 1 on, one mantissa bit is kept and the step is 2^(e-1) for a in
-// [2^e, 2^(e+1)).  (A branch-free form that computes both cases measured slower: whole
-// waves usually take one branch.)
+// (k + 1/2) / 2^16 < (a - lo) / (hi - lo), evaluated as 2k + 1 < (t - floor t) * 2^17 with
+// t = a / step.  The grid step is 1/2 below 2 and 2^(e-1) for a in [2^e, 2^(e+1)), e >= 1,
+// i.e. 2^(E - 128) with E = max(biased exponent of a, 127); t = ldexp(a, 128 - E) lies in
+// [0, 4) and floor t is the lower neighbour's position on the step grid, so the code of lo
+// is floor t + 2 (E - 127).  Every quantity is exact in binary32 (a power-of-two scaling,
+// t - floor t by Sterbenz, 2k + 1 < 2^17), so the comparison decides exactly as the
+// definition; one formula for all binades keeps the lanes of a wave on one path.
 __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t k) {
   if (!(a < kE2M1Max)) return 7u;
-  uint32_t lo_code;
-  float lo, inv17;
-  if (a < 1.0f) {
-    lo_code = (uint32_t)(a + a);            // truncation: 0 or 1
-    lo = (float)lo_code * 0.5f;
-    inv17 = 262144.0f;                      // 2^17 / (1/2)
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    lo = __uint_as_float(b & 0xFFC00000u);  // truncate to 1 mantissa bit
-    lo_code = (b >> 22) - 252u;             // 1.0 -> code 2
-    // 2^17 / 2^(e-1) = 2^(18-e), from the exponent field E = e + 127
-    inv17 = __uint_as_float((272u - ((b >> 23) & 0xFFu)) << 23);
-  }
-  return lo_code + ((float)(2u * k + 1u) < (a - lo) * inv17 ? 1u : 0u);
+  const uint32_t e = max(__float_as_uint(a) >> 23, 127u);
+  const float t = __builtin_amdgcn_ldexpf(a, 128 - (int)e);
+  const float q = __builtin_floorf(t);
+  const uint32_t lo_code = (uint32_t)q + 2u * (e - 127u);
+  return lo_code + ((float)(2u * k + 1u) < (t - q) * 131072.0f ? 1u : 0u);
 }
 
 // Nearest-even E2M1 codes of 16 values y[j] * rr, packed two per byte (element 2i in

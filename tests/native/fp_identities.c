@@ -8,6 +8,13 @@
  *  3. quarter: RN(RN(t / 4) * r) == RN(t * RN(r / 4)) when |t| >= 2^-124 and
  *             r >= 2^-124, and both are below 2^-18 in magnitude, with the sign of t,
  *             when |t| < 2^-124 and r < 2^108 (random pairs).
+ *  4. srstep: the stochastic E2M1 magnitude code of the kernels, lo + [2k + 1 <
+ *             (t - floor t) 2^17] with t = ldexp(a, 128 - max(E, 127)) (E the biased
+ *             exponent of a) and lo = floor t + 2 (max(E, 127) - 127), equals the
+ *             definition -- round up iff (k + 1/2) / 2^16 < (a - lo) / (hi - lo) on the
+ *             E2M1 grid, evaluated in binary64 -- for every 5th binary32 in [0, 6) with a
+ *             hashed 16-bit k, and for values placed exactly on, and one ulp around, the
+ *             decision point of random (grid cell, k).
  * Prints one line per identity: "<name> <checked> <mismatches>".  Built with
  * -ffp-contract=off so that every operation rounds on its own. */
 #include <math.h>
@@ -32,6 +39,28 @@ static float rand_finite(uint64_t *s) {
   if (((z >> 48) & 63u) == 0) m = 0;          /* some exact powers of two and zeros */
   if (((z >> 54) & 63u) == 0) { e = 0; m = 0; }
   return f_of((sg << 31) | (e << 23) | m);
+}
+
+/* E2M1 magnitudes of codes 0..7 */
+static const double E2M1_G[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* stochastic code by the definition, a in [0, 6) */
+static unsigned sr_definition(float a, uint32_t k) {
+  unsigned lo = 0;
+  for (unsigned c = 1; c < 8; ++c)
+    if (E2M1_G[c] <= (double)a) lo = c;
+  const double frac = ((double)a - E2M1_G[lo]) / (E2M1_G[lo + 1] - E2M1_G[lo]);
+  return ((double)k + 0.5) / 65536.0 < frac ? lo + 1 : lo;
+}
+
+/* the kernels' formula, a in [0, 6) */
+static unsigned sr_kernel(float a, uint32_t k) {
+  uint32_t e = u_of(a) >> 23;
+  if (e < 127u) e = 127u;
+  const float t = ldexpf(a, 128 - (int)e);
+  const float q = floorf(t);
+  const unsigned lo = (unsigned)q + 2u * (e - 127u);
+  return lo + ((float)(2u * k + 1u) < (t - q) * 131072.0f ? 1u : 0u);
 }
 
 int main(void) {
@@ -78,5 +107,29 @@ int main(void) {
     ++n;
   }
   printf("quarter %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+
+  bad = 0; n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+  for (int64_t ui = 0; ui < 0x40C00000; ui += 5) {
+    uint64_t hs = (uint64_t)ui * 0x9E3779B97F4A7C15ull;
+    const uint32_t k = (uint32_t)(splitmix(&hs) & 0xFFFFu);
+    const float a = f_of((uint32_t)ui);
+    bad += sr_kernel(a, k) != sr_definition(a, k);
+    ++n;
+  }
+  for (int i = 0; i < 4000000; ++i) {
+    const uint64_t z = splitmix(&s);
+    const int cell = (int)(z % 7u);                 /* grid cell [G[cell], G[cell + 1]) */
+    const uint32_t k = (uint32_t)(z >> 8) & 0xFFFFu;
+    const double lo = E2M1_G[cell], hi = E2M1_G[cell + 1];
+    const float a0 = (float)(lo + (hi - lo) * ((double)k + 0.5) / 65536.0);   /* exact */
+    for (int d = -1; d <= 1; ++d) {
+      const float a = f_of(u_of(a0) + (uint32_t)d);
+      if (!(a >= 0.0f && a < 6.0f)) continue;
+      bad += sr_kernel(a, k) != sr_definition(a, k);
+      ++n;
+    }
+  }
+  printf("srstep %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
   return 0;
 }

@@ -3,7 +3,8 @@
 The kernels (1) divide a block amax by 6 with a product and one FMA correction instead
 of a division, (2) take the tensor amax after the RHT without forming the last butterfly
 stage, using max(|a+b|, |a-b|) = |a| + |b| under monotonic rounding, and (3) fold the
-RHT's final 1/4 into the block multiplier.  Each shortcut must give bit-identical
+RHT's final 1/4 into the block multiplier; and (4) encode stochastic rounding with one
+formula for every binade of the E2M1 grid.  Each shortcut must give bit-identical
 results to the plain form that the oracle evaluates (RHT and scale steps of the NVIDIA
 developer blog "NVFP4 trains with precision of 16-bit ...", section on the pre-training
 quantization recipe).  These are properties of IEEE binary32 arithmetic, checked here on
@@ -46,3 +47,9 @@ def test_absadd_max(results):
 def test_quarter_fold(results):
     n, bad = results["quarter"]
     assert n > 10_000_000 and bad == 0
+
+
+def test_stochastic_code_formula(results):
+    # the kernels' single-formula stochastic E2M1 code against the rounding definition
+    n, bad = results["srstep"]
+    assert n > 200_000_000 and bad == 0
