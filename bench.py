@@ -6,15 +6,17 @@ path once:
   quantize W   5120 x 20480 bf16 weight, 16x16 blocks, W and W^T codes from one read
   GEMM         C = X_q . (W^T)_q^T, 8192 x 20480 x 5120, fp32 accumulate, bf16 out
   dequantize   X_q -> bf16
-Inputs are seeded synthetic tensors resident in HBM before timing starts.  The printed
-JSON line carries the step throughput (GEMM FLOP per step / step time), per-kernel
-times from HIP events recorded on the launch stream, the roofline of the dominant
-kernel, standalone quantize figures for workloads 2-4 (input buffers rotated so the
+Inputs are seeded synthetic tensors resident in HBM before timing starts.  The timed
+steps are replays of a HIP graph of one step, so the step time is GPU time.  The printed
+JSON line carries the step throughput (GEMM FLOP per step / step time), per-kernel times
+(HIP events around a graph of back-to-back launches of that kernel, on the stream it runs
+on), the roofline of the dominant kernel, standalone quantize figures for workloads 2-4 (input buffers rotated so the
 256 MB Infinity Cache cannot hold them), the MXFP4 variant (quantize, and the GEMM on the
 native scaled FP4 MFMA), one linear-layer training step (Fprop, Dgrad, Wgrad), and the
 CPU oracle's rate on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-micro]
+    python bench.py --summarize ROCPROF_DIR [--last N]   (summary of a rocprofv3 csv run)
 """
 from __future__ import annotations
 
@@ -76,6 +78,12 @@ def parse():
     ap.add_argument("--context", action="store_true", help="also time torch fp16 matmul")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print the summary of a rocprofv3 output directory (kernel trace "
+                         "and/or counters) instead of benchmarking")
+    ap.add_argument("--last", type=int, default=0,
+                    help="with --summarize: only the last N dispatches of each kernel and "
+                         "grid (the timed ones of a run with --steps N)")
     return ap.parse_args()
 
 
@@ -86,27 +94,6 @@ def log(msg):
 def to_dev(x_u16):
     import torch
     return torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16)).view(torch.bfloat16).cuda()
-
-
-class Timer:
-    """Accumulates HIP-event time of named launches on the current stream."""
-
-    def __init__(self):
-        self.ev = {}
-
-    def run(self, name, fn):
-        import torch
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        r = fn()
-        b.record()
-        self.ev.setdefault(name, []).append((a, b))
-        return r
-
-    def avg_ms(self, name):
-        pairs = self.ev[name]
-        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
 def copy_bandwidth(nbuf_bytes=512 << 20, chunk=84 << 20, iters=30):
@@ -316,6 +303,14 @@ def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
     from block_scaled_fp4_06_amd import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     cores = min(threads, os.cpu_count() or 1)
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     xs = np.ascontiguousarray(x_np[:sample_rows])
     steps, work = [], 0.0
     for _ in range(repeats):
@@ -370,15 +365,143 @@ def cpu_baseline(x_np, w_np, sample_rows=M, repeats=5):
     what = ("the whole step (all %d activation rows)" % M if sample_rows == M else
             "%d of %d activation rows, scaled to one step" % (sample_rows, M))
     return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
             "sample": "%s: quantize X (RHT, 1x16), quantize W and W^T (16x16), binary64 GEMM, "
                       "dequantize X; median of %d runs, %.1f s of CPU work in all"
                       % (what, repeats, work),
             "seconds_per_step_est": round(t_step, 2), **rates}
 
 
+def _csv_rows(pattern_dir, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(pattern_dir, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _field(row, *names):
+    for n in names:
+        v = row.get(n)
+        if v not in (None, ""):
+            return v
+    return None
+
+
+def _kernel_key(row):
+    name = _field(row, "Kernel_Name") or "?"
+    grid = int(_field(row, "Grid_Size_X", "Grid_Size") or 0)
+    wg = int(_field(row, "Workgroup_Size_X", "Workgroup_Size") or 0)
+    return name, grid, wg
+
+
+def summarize(d, last=0):
+    """Summary of a rocprofv3 ``--output-format csv`` directory.
+
+    Kernel trace: per kernel and grid size, the dispatch durations in us (mean, median,
+    p10, p90, min, max).  Counters: per kernel and grid size, the median over dispatches of
+    each counter summed over its instances; FETCH_SIZE and WRITE_SIZE are also given in MB,
+    scaled by what they read for the 256 MiB device copy of ``--copy-calibration`` when that
+    copy is in the run.  ``last`` > 0 keeps only the last `last` dispatches of each kernel
+    and grid, in dispatch order (the timed graph replay of a run with ``--steps last``)."""
+    out = []
+    trace = _csv_rows(d, "kernel_trace.csv")
+    if trace:
+        groups = {}
+        for r in trace:
+            t0, t1 = int(_field(r, "Start_Timestamp")), int(_field(r, "End_Timestamp"))
+            groups.setdefault(_kernel_key(r), []).append((t0, (t1 - t0) / 1000.0))
+        out.append("rocprofv3 kernel trace: durations in us%s" %
+                   (", last %d dispatches of each kernel and grid" % last if last else ""))
+        out.append("%-46s %9s %5s %6s %10s %10s %10s %10s %10s %10s" % (
+            "kernel", "grid_thr", "wg", "calls", "mean", "median", "p10", "p90", "min", "max"))
+        rows = []
+        for (name, grid, wg), v in groups.items():
+            v.sort()
+            us = np.array([x[1] for x in v][-last:] if last else [x[1] for x in v])
+            rows.append((us.sum(), name, grid, wg, us))
+        for _, name, grid, wg, us in sorted(rows, key=lambda t: -t[0]):
+            p10, med, p90 = np.percentile(us, [10, 50, 90])
+            out.append("%-46s %9d %5d %6d %10.2f %10.2f %10.2f %10.2f %10.2f %10.2f" % (
+                name[:46], grid, wg, us.size, us.mean(), med, p10, p90, us.min(), us.max()))
+    ctr = _csv_rows(d, "counter_collection.csv")
+    if ctr:
+        per = {}   # (kernel key) -> dispatch -> counter -> summed value
+        order = {}
+        for r in ctr:
+            key, disp = _kernel_key(r), int(_field(r, "Dispatch_Id", "Correlation_Id") or 0)
+            cname = _field(r, "Counter_Name")
+            per.setdefault(key, {}).setdefault(disp, {})
+            per[key][disp][cname] = per[key][disp].get(cname, 0.0) + float(_field(r, "Counter_Value"))
+        names = sorted({c for k in per.values() for dd in k.values() for c in dd})
+        scale = {}
+        copies = [(dd.get(c, 0.0), c) for (n, _, _), k in per.items() if "copyBuffer" in n
+                  for dd in k.values() for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            top = max([v for v, cc in copies if cc == c] or [0.0])
+            if top > 100_000:   # only the 256 MiB calibration copy reaches 100 MB (KiB)
+                scale[c] = (256 << 20) / 1024.0 / top
+        out.append("")
+        out.append("rocprofv3 counters: median per dispatch%s; counters summed over instances" %
+                   (", last %d dispatches" % last if last else ""))
+        for c, f in scale.items():
+            out.append("calibration: %s counts %.4f of the bytes the 256 MiB copy moves "
+                       "(scale x%.4f)" % (c, 1.0 / f, f))
+        hdr = "%-46s %9s %5s" % ("kernel", "grid_thr", "n")
+        for c in names:
+            hdr += " %16s" % c
+            if c in scale:
+                hdr += " %10s" % (c.split("_")[0].lower() + "_MB")
+        out.append(hdr)
+        for key in sorted(per, key=lambda k: k[0]):
+            ds = [per[key][dd] for dd in sorted(per[key])]
+            if last:
+                ds = ds[-last:]
+            line = "%-46s %9d %5d" % (key[0][:46], key[1], len(ds))
+            for c in names:
+                med = float(np.median([dd.get(c, 0.0) for dd in ds]))
+                line += " %16.6g" % med
+                if c in scale:
+                    line += " %10.2f" % (med * 1024.0 * scale[c] / 1e6)
+            out.append(line)
+    if not out:
+        out.append("no kernel_trace.csv or counter_collection.csv under %s" % d)
+    return "\n".join(out)
+
+
+def graph_of(fn, calls):
+    """A HIP graph of `calls` back-to-back invocations of fn (captured on a side stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for _ in range(calls):
+            fn()
+    return g
+
+
+def replay_ms(g, reps=1):
+    """Event-timed milliseconds of `reps` replays of graph g on the current stream (the
+    replay launches there), after one untimed replay."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize, args.last))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -392,45 +515,49 @@ def main():
     w_np = W.w5_weight()
     X = to_dev(x_np)
     Wd = to_dev(w_np)
-    qx = N.quantize(X, rht=True, rht_seed=W.RHT_SEED)
-    qw = N.quantize(Wd, blocking="16x16", with_transpose=True)
+    dev = X.device
+    # workspaces made before any capture (a zero-fill recorded in a graph would rerun on
+    # every replay); the two quantizations run in stream order and share one
+    ws_q = N.new_workspace(dev)
+    ws_g = N.new_gemm_workspace(dev)
+    qx = N.quantize(X, rht=True, rht_seed=W.RHT_SEED, workspace=ws_q)
+    qw = N.quantize(Wd, blocking="16x16", with_transpose=True, workspace=ws_q)
+    qwt = qw.transposed()
     C = torch.empty((M, NN), dtype=torch.bfloat16, device="cuda")
     Xh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
 
-    def step(t=None):
-        run = (lambda n, f: t.run(n, f)) if t is not None else (lambda n, f: f())
-        run("quantize_x", lambda: N.quantize(X, rht=True, rht_seed=W.RHT_SEED, out=qx))
-        run("quantize_w", lambda: N.quantize(Wd, blocking="16x16", with_transpose=True, out=qw))
-        run("gemm", lambda: N.gemm(qx, qw.transposed(), out=C))
-        run("dequantize_x", lambda: N.dequantize(qx, torch.bfloat16, out=Xh))
+    calls = {
+        "quantize_x": lambda: N.quantize(X, rht=True, rht_seed=W.RHT_SEED, out=qx, workspace=ws_q),
+        "quantize_w": lambda: N.quantize(Wd, blocking="16x16", with_transpose=True, out=qw,
+                                         workspace=ws_q),
+        "gemm": lambda: N.gemm(qx, qwt, out=C, workspace=ws_g),
+        "dequantize_x": lambda: N.dequantize(qx, out=Xh),
+    }
+
+    def step():
+        for fn in calls.values():
+            fn()
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(args.steps):
-        step()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
-    # per-kernel times: a second timed pass with events between the launches
-    tm = Timer()
-    for _ in range(args.steps):
-        step(tm)
-    torch.cuda.synchronize()
+    # the timed steps replay a captured graph of one step: the four launches run back to
+    # back, so ms_per_step is GPU time, not the host's per-call cost
+    g_step = graph_of(step, 1)
+    log("timing %d steps (graph replays)" % args.steps)
+    ms = replay_ms(g_step, args.steps) / args.steps
+    # per-kernel times: a graph of `steps` back-to-back launches of one kernel, replayed
+    # once untimed and once timed (the last `steps` dispatches of each kernel in a trace of
+    # this run are the timed ones)
     kern = {}
     flops = 2.0 * M * NN * K
     for name, by, unit in (("quantize_x", quant_bytes(M, K, "1x16"), "GB/s"),
                            ("quantize_w", quant_bytes(K, NN, "16x16", True), "GB/s"),
                            ("gemm", flops, "TFLOP/s"),
                            ("dequantize_x", dequant_bytes(M, K, "1x16"), "GB/s")):
-        t = tm.avg_ms(name)
+        t = replay_ms(graph_of(calls[name], args.steps)) / args.steps
         if unit == "GB/s":
             ach = by / (t * 1e-3) / 1e9
             kern[name] = {"ms": round(t, 4), "GBps": round(ach, 1),
@@ -495,6 +622,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
         out["cpu_baseline"] = cpu_baseline(x_np, w_np)
+    torch.cuda.synchronize()   # nothing of ours is in flight when the process exits
     print(json.dumps(out), flush=True)
 
 

@@ -27,7 +27,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // hardware conversion (scale 1.0, exact), then (e2m1 * sbd) * s.
 template <int B>
 __device__ __forceinline__ void decode_byte(uint32_t w, float sbd, float s, float *v) {
-  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  const float2_t f = e2m1_decode_pair<B>(w);
   v[0] = (f[0] * sbd) * s;   // first product exact
   v[1] = (f[1] * sbd) * s;
 }

@@ -24,8 +24,6 @@
 namespace nvfp4 {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
@@ -62,33 +60,7 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t *p, int left) {
   return v;
 }
 
-// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times the block
-// scale sbd, as eight fp16 values.  Exact: e2m1 * e4m3 fits fp16.
-template <bool HWCVT>
-__device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 sbd) {
-  half8_t r;
-  if (HWCVT) {
-    const half2_t s2 = {sbd, sbd};
-    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-    r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
-    r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t q = (w >> (4 * j)) & 0xFu, m = q & 7u;
-      // fp16 bits of the E2M1 magnitude: 0.5 -> 0x3800; m >= 2 -> exponent (m>>1)+14
-      const uint32_t mag = m == 0u ? 0u : (m == 1u ? 0x3800u : ((((m >> 1) + 14u) << 10) | ((m & 1u) << 9)));
-      const uint16_t bits = (uint16_t)(mag | ((q & 8u) << 12));
-      r[j] = __builtin_bit_cast(_Float16, bits) * sbd;
-    }
-  }
-  return r;
-}
-
-template <bool F32, bool K32, bool HWCVT>
+template <bool F32, bool K32>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kLdsStride];
@@ -142,10 +114,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p, int tiles_n) {
       const uint4 c = *reinterpret_cast<const uint4 *>(sA + row * kLdsStride + 16 * h);
       const _Float16 s0 = (_Float16)e4m3_decode(sAs[row * 4 + 2 * h]);
       const _Float16 s1 = (_Float16)e4m3_decode(sAs[row * 4 + 2 * h + 1]);
-      aop[i][0] = dequant8<HWCVT>(c.x, s0);
-      aop[i][1] = dequant8<HWCVT>(c.y, s0);
-      aop[i][2] = dequant8<HWCVT>(c.z, s1);
-      aop[i][3] = dequant8<HWCVT>(c.w, s1);
+      aop[i][0] = dequant8_f16(c.x, s0);
+      aop[i][1] = dequant8_f16(c.y, s0);
+      aop[i][2] = dequant8_f16(c.z, s1);
+      aop[i][3] = dequant8_f16(c.w, s1);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -153,10 +125,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p, int tiles_n) {
       const uint4 c = *reinterpret_cast<const uint4 *>(sB + row * kLdsStride + 16 * h);
       const _Float16 s0 = (_Float16)e4m3_decode(sBs[row * 4 + 2 * h]);
       const _Float16 s1 = (_Float16)e4m3_decode(sBs[row * 4 + 2 * h + 1]);
-      bop[j][0] = dequant8<HWCVT>(c.x, s0);
-      bop[j][1] = dequant8<HWCVT>(c.y, s0);
-      bop[j][2] = dequant8<HWCVT>(c.z, s1);
-      bop[j][3] = dequant8<HWCVT>(c.w, s1);
+      bop[j][0] = dequant8_f16(c.x, s0);
+      bop[j][1] = dequant8_f16(c.y, s0);
+      bop[j][2] = dequant8_f16(c.z, s1);
+      bop[j][3] = dequant8_f16(c.w, s1);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -213,11 +185,6 @@ constexpr int kScalesB2 = kT2 * 16;      // 4 KB per operand per stage
 constexpr int kStageB2 = 2 * kCodesB2 + 2 * kScalesB2;
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-
-__device__ __forceinline__ half2_t scale_pair(uint32_t w, int h) {
-  // two E4M3 bytes (2h, 2h+1) of w -> two fp16, exact (scale 1.0)
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * h), 1.0f, false);
-}
 
 // Work items.  Workgroups 0 .. t_dp-1 each compute one whole tile (t_dp is all tiles, or
 // the tiles of the full rounds when the last round would leave CUs idle).  With a
@@ -352,8 +319,8 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
       cb[b][i] = lds16(st + kCodesB2 + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
       const uint32_t wa = *reinterpret_cast<const uint32_t *>(ssa + j * 1024 + (wm * 128 + i * 32 + l32) * 4);
       const uint32_t wb = *reinterpret_cast<const uint32_t *>(ssb + j * 1024 + (wn * 128 + i * 32 + l32) * 4);
-      hsa[b][i] = scale_pair(wa, h);
-      hsb[b][i] = scale_pair(wb, h);
+      hsa[b][i] = e4m3_pair_f16(wa, h);
+      hsb[b][i] = e4m3_pair_f16(wb, h);
     }
   };
   auto dequant_step = [&](int s, half8_t (&ad)[4], half8_t (&bd)[4]) {
@@ -362,8 +329,8 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
     for (int i = 0; i < 4; ++i) {
       const uint32_t wa = q == 0 ? ca[b][i].x : q == 1 ? ca[b][i].y : q == 2 ? ca[b][i].z : ca[b][i].w;
       const uint32_t wb = q == 0 ? cb[b][i].x : q == 1 ? cb[b][i].y : q == 2 ? cb[b][i].z : cb[b][i].w;
-      ad[i] = dequant8<true>(wa, hsa[b][i][q >> 1]);
-      bd[i] = dequant8<true>(wb, hsb[b][i][q >> 1]);
+      ad[i] = dequant8_f16(wa, hsa[b][i][q >> 1]);
+      bd[i] = dequant8_f16(wb, hsb[b][i][q >> 1]);
     }
   };
 
@@ -486,8 +453,7 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + off;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)(acc[i][jj][r] * alpha)),
-                                        dst + jj * 32);
+            __builtin_nontemporal_store(bf16_bits_rn(acc[i][jj][r] * alpha), dst + jj * 32);
         }
       }
     return;
@@ -565,16 +531,12 @@ hipError_t launch_gemm(const GemmLaunch &g, hipStream_t stream) {
   const int tiles_n = (int)((g.N + kBN - 1) / kBN);
   const unsigned grid = (unsigned)(tiles_n * ((g.M + kBM - 1) / kBM));
   const bool k32 = (g.K % 32) == 0;
-#ifndef NVFP4_GEMM_HWCVT
-#define NVFP4_GEMM_HWCVT 1
-#endif
-  constexpr bool hw = NVFP4_GEMM_HWCVT != 0;
   if (g.out_f32) {
-    if (k32) gemm_kernel<true, true, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
-    else gemm_kernel<true, false, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
+    if (k32) gemm_kernel<true, true><<<grid, 256, 0, stream>>>(p, tiles_n);
+    else gemm_kernel<true, false><<<grid, 256, 0, stream>>>(p, tiles_n);
   } else {
-    if (k32) gemm_kernel<false, true, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
-    else gemm_kernel<false, false, hw><<<grid, 256, 0, stream>>>(p, tiles_n);
+    if (k32) gemm_kernel<false, true><<<grid, 256, 0, stream>>>(p, tiles_n);
+    else gemm_kernel<false, false><<<grid, 256, 0, stream>>>(p, tiles_n);
   }
   return hipGetLastError();
 }

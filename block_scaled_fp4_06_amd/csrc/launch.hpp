@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "nvfp4.h"
+
 namespace nvfp4 {
 
 // Quantization workspace: a block of coordination words, then one 64-bit word per chunk of
@@ -11,8 +13,26 @@ namespace nvfp4 {
 constexpr size_t kCoordBytes = 8192;
 constexpr size_t kWorkspaceBytes = ((size_t)8 << 20) + kCoordBytes;
 
-// Chunks the quantization kernel divides a rows x cols tensor into.
-uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding);
+// Work division of the quantization kernels (quantize.hip), shared with the argument checks.
+// 1x16, nearest-even: a chunk is kT1 threads x kG1 row groups of 16 elements.
+constexpr int kT1 = 512;
+constexpr int kG1 = 20;
+constexpr uint32_t kChunk1 = (uint32_t)kT1 * kG1;
+// 1x16, stochastic: pass 1 writes one 32-bit partial maximum per workgroup.
+constexpr uint32_t kAmaxMaxWg = 1024;
+// 16x16: a chunk is up to kG16 tile-rows x 16 tile-columns.
+constexpr int kG16 = 8;
+
+// 64-bit words the quantization workspace needs after its header for a rows x cols tensor
+// (rows, cols >= 0, multiples of 16, rows * cols <= 2^35): one per chunk, or the pass-1
+// partials of stochastic rounding with 1x16 blocks.
+inline uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding) {
+  if (blocking == 0) {
+    if (rounding == 1) return (kAmaxMaxWg * 4 + 7) / 8;
+    return ((uint64_t)rows * (uint64_t)(cols / 16) + kChunk1 - 1) / kChunk1;
+  }
+  return (((uint64_t)(rows / 16) + kG16 - 1) / kG16) * (((uint64_t)(cols / 16) + 15) / 16);
+}
 
 struct QuantLaunch {
   const uint16_t *x;
@@ -31,6 +51,13 @@ struct QuantLaunch {
 };
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
+
+// The argument checks of nvfp4_quantize other than its workspace (api.hip); on success
+// fills q, with q->ws = nullptr.  Makes no HIP call.
+nvfp4_status check_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                            const nvfp4_quant_params *p, uint8_t *codes, uint8_t *scales,
+                            float *global_dec, uint8_t *codes_t, uint8_t *scales_t,
+                            uint32_t *dev_status, QuantLaunch *q);
 
 
 struct DequantLaunch {

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kQT) void mx_quant_kernel(const uint16_t *__restric
 // exact in bf16, so the bf16 output is the top half of the binary32 pattern.
 template <int B>
 __device__ __forceinline__ void mx_decode_byte(uint32_t c, int e, float *v) {
-  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, B);   // exact
+  const float2_t f = e2m1_decode_pair<B>(c);   // exact
   v[2 * B] = __builtin_ldexpf(f[0], e);
   v[2 * B + 1] = __builtin_ldexpf(f[1], e);
 }
@@ -449,7 +449,7 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           *reinterpret_cast<uint16_t *>(ob + row * kOutStride + (jj * 32 + l32) * 2) =
-              __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][r]);
+              bf16_bits_rn(acc[i][jj][r]);
         }
     const int crow = lane >> 4, cchunk = lane & 15;
     uint16_t *cdst = reinterpret_cast<uint16_t *>(p.c) + (int64_t)(m0 + wm * 128 + crow) * p.ldc +
@@ -474,7 +474,7 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
         } else {
           uint16_t *dst = reinterpret_cast<uint16_t *>(p.c) + off;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) dst[jj * 32] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][r]);
+          for (int jj = 0; jj < 4; ++jj) dst[jj * 32] = bf16_bits_rn(acc[i][jj][r]);
         }
       }
     return;
@@ -490,7 +490,7 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
         if (row < p.M && col < p.N) {
           const int64_t off = (int64_t)row * p.ldc + col;
           if (F32) reinterpret_cast<float *>(p.c)[off] = acc[i][jj][r];
-          else reinterpret_cast<uint16_t *>(p.c)[off] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][jj][r]);
+          else reinterpret_cast<uint16_t *>(p.c)[off] = bf16_bits_rn(acc[i][jj][r]);
         }
       }
 }

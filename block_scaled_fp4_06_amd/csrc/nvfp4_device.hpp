@@ -155,6 +155,45 @@ __device__ __forceinline__ uint2 e2m1_rn_pack16(const float y[16], float rr) {
   return make_uint2(lo, hi);
 }
 
+// ---------------------------------------------------------------- decoding
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// The two E2M1 codes of byte B of w (low nibble first) as fp32, exact: the hardware fp4
+// conversion with scale 1.0.
+template <int B>
+__device__ __forceinline__ float2_t e2m1_decode_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times the block
+// scale sbd, as eight fp16 values: the hardware fp4 -> fp16 conversion with scale 1.0, then
+// a packed fp16 multiply.  Exact: every e2m1 * e4m3 product fits fp16 (at most 6
+// significant bits, magnitudes 2^-10 .. 2688).
+__device__ __forceinline__ half8_t dequant8_f16(uint32_t w, _Float16 sbd) {
+  const half2_t s2 = {sbd, sbd};
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  half8_t r;
+  r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+  r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
+  return r;
+}
+
+// E4M3 bytes 2h and 2h+1 of w as two fp16 values (exact: the hardware fp8 -> fp16
+// conversion with scale 1.0; every E4M3 value is an fp16 value).
+__device__ __forceinline__ half2_t e4m3_pair_f16(uint32_t w, int h) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * h), 1.0f, false);
+}
+
+// bf16 bit pattern of v, nearest-even (the hardware conversion; NaN stays NaN).
+__device__ __forceinline__ uint16_t bf16_bits_rn(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
 struct Philox4 { uint32_t x, y, z, w; };

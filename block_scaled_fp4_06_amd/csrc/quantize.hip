@@ -330,9 +330,6 @@ __device__ __forceinline__ uint4 mask4(const uint4 &v, uint32_t m) {
 // ---------------------------------------------------------------- 1x16
 // A chunk is kG1 * kT1 consecutive row groups; thread t holds groups base + i*kT1 + t,
 // i < kG1, so every load and store instruction of a wave covers consecutive memory.
-constexpr int kT1 = 512;
-constexpr int kG1 = 20;
-constexpr uint32_t kChunk1 = (uint32_t)kT1 * kG1;
 
 // Two waves per SIMD (one workgroup per CU): up to 256 registers per lane for the chunk.
 // Nearest-even rounding only.
@@ -466,7 +463,6 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 //   pass 2  quant_1x16_sr_kernel: every workgroup reduces the partials and encodes its
 //           range, eight resident workgroups per CU.
 constexpr int kThreads = 256;
-constexpr uint32_t kAmaxMaxWg = 1024;   // pass-1 workgroups (each writes one partial)
 constexpr uint32_t kSrMaxWg = 2048;     // pass-2 workgroups: eight per CU
 
 // pass 1
@@ -597,7 +593,6 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
 // G = 8 holds 64 MiB on chip (four workgroups per CU); a tensor that fits on chip in
 // chunks of G = 4 (five or six per CU) takes them: small tensors get twice the workgroups.
 constexpr int kT16 = 256;
-constexpr int kG16 = 8;
 template <bool RHT, bool SR, bool TRANS, int G>
 __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t rk0,
@@ -778,14 +773,6 @@ uint32_t resident_grid(int threads) {
 }
 
 }  // namespace
-
-uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding) {
-  if (blocking == 0) {
-    if (rounding == 1) return (kAmaxMaxWg * 4 + 7) / 8;   // pass-1 partials
-    return ceil_div((uint64_t)rows * (uint64_t)(cols / 16), kChunk1);
-  }
-  return ceil_div((uint64_t)(rows / 16), kG16) * ceil_div((uint64_t)(cols / 16), 16);
-}
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
   const bool rht = q.rht != 0, sr = q.rounding == 1;

@@ -10,6 +10,7 @@ Low-level functions carry the C names (``nvfp4_quantize`` ...) and take raw poin
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from dataclasses import dataclass
@@ -45,7 +46,8 @@ class NVFP4Error(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, nvfp4_status_string(status), status))
 
 
-EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_dequantize",
+EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
+            "nvfp4_dequantize",
             "nvfp4_gemm", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_transpose_bf16", "mxfp4_quantize", "mxfp4_dequantize",
             "mxfp4_gemm",
             "nvfp4_status_string", "nvfp4_abi_version")
@@ -185,7 +187,81 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _check_buffer(name, t, shape, dtypes, device, row_major=True):
+    """Raise ValueError unless tensor t has the given shape, one of `dtypes` and `device`,
+    and (row_major) unit column stride with a row stride of at least its width: the layout
+    the library writes or reads through the raw pointer."""
+    if t is None:
+        raise ValueError("%s is missing" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if row_major and len(shape) == 2 and shape[0] > 0 and shape[1] > 0:
+        if t.stride(1) != 1 or t.stride(0) < shape[1]:
+            raise ValueError("%s must be row-major with unit column stride" % name)
+    elif not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _require_gpu(device):
+    """The last check before a library call: every buffer lives on this GPU device."""
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, not %s" % device)
+
+
+def _check_workspace(ws, need, device):
+    import torch
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError("workspace has %d bytes, needs %d" % (ws.numel(), need))
+    if ws.device != device:
+        raise ValueError("workspace is on %s, expected %s" % (ws.device, device))
+
+
+def _check_nvfp4(name, q, device=None):
+    """The buffers of an NVFP4Tensor have the documented shapes, dtypes and one device."""
+    import torch
+    device = q.codes.device if device is None else device
+    if q.blocking not in (BLOCK_1x16, BLOCK_16x16):
+        raise ValueError("%s.blocking must be 0 (1x16) or 1 (16x16)" % name)
+    sshape = (q.rows // 16, q.cols // 16) if q.blocking == BLOCK_16x16 else (q.rows, q.cols // 16)
+    u8 = (torch.uint8,)
+    _check_buffer(name + ".codes", q.codes, (q.rows, q.cols // 2), u8, device, False)
+    _check_buffer(name + ".scales", q.scales, sshape, u8, device, False)
+    _check_buffer(name + ".global_dec", q.global_dec, (1,), (torch.float32,), device, False)
+
+
+def _out_dtypes():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
 _WORKSPACES = {}
+_GEMM_WORKSPACES = {}
+
+
+def release_workspaces():
+    """Wait for the work queued on every device that holds a cached workspace, then drop
+    the cached workspaces (one quantize and one GEMM workspace per (device, stream)).  Runs
+    at interpreter exit, so the tensors go back to torch while its allocator and the HIP
+    runtime are still up and no launch of ours is in flight when the process ends."""
+    devices = {k[0] for k in list(_WORKSPACES) + list(_GEMM_WORKSPACES)}
+    if devices:
+        import torch
+        for d in devices:
+            try:
+                torch.cuda.synchronize(d)
+            except RuntimeError:
+                pass
+    _WORKSPACES.clear()
+    _GEMM_WORKSPACES.clear()
+
+
+atexit.register(release_workspaces)
 
 
 def new_workspace(device):
@@ -230,6 +306,23 @@ def quantize(x, blocking="1x16", rounding="rne", rht=False, rht_seed=0, sr_seed=
             ct = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
             st_ = torch.empty((cols // 16, rows // 16), dtype=torch.uint8, device=dev)
         out = NVFP4Tensor(codes, scales, g, rows, cols, blk, ct, st_, st)
+    else:
+        if (out.rows, out.cols, out.blocking) != (rows, cols, blk):
+            raise ValueError("out was made for a %dx%d tensor with blocking %d" %
+                             (out.rows, out.cols, out.blocking))
+        _check_nvfp4("out", out, dev)
+        if with_transpose != (out.codes_t is not None) or (out.codes_t is None) != (out.scales_t is None):
+            raise ValueError("out.codes_t/scales_t must be given exactly when with_transpose")
+        if out.codes_t is not None:
+            _check_buffer("out.codes_t", out.codes_t, (cols, rows // 2), (torch.uint8,), dev, False)
+            _check_buffer("out.scales_t", out.scales_t, (cols // 16, rows // 16), (torch.uint8,),
+                          dev, False)
+        if out.status is not None:
+            _check_buffer("out.status", out.status, tuple(out.status.shape), (torch.int32,), dev,
+                          False)
+    if workspace is not None:
+        _check_workspace(workspace, nvfp4_quantize_workspace_bytes(), dev)
+    _require_gpu(dev)
     sh = _stream(stream, dev)
     ws = workspace if workspace is not None else _workspace(dev, sh.value)
     prm = QuantParams(blk, _ROUNDING[rounding], 1 if rht else 0, 0, rht_seed, sr_seed,
@@ -243,10 +336,15 @@ def quantize(x, blocking="1x16", rounding="rne", rht=False, rht_seed=0, sr_seed=
 
 
 def dequantize(q: NVFP4Tensor, out_dtype=None, stream=None, out=None):
+    """x = e2m1(code) * e4m3(scale) * global as a (rows, cols) float32 or bf16 tensor; `out`
+    (optional) must have that shape and dtype, unit column stride, on the codes' device."""
     import torch
-    out_dtype = out_dtype or torch.bfloat16
+    _check_nvfp4("q", q)
     if out is None:
-        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype or torch.bfloat16,
+                          device=q.codes.device)
+    _check_buffer("out", out, (q.rows, q.cols), _out_dtypes(), q.codes.device)
+    _require_gpu(q.codes.device)
     od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     rc = nvfp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.global_dec), q.rows, q.cols,
                           q.blocking, _ptr(out), out.stride(0), od,
@@ -254,9 +352,6 @@ def dequantize(q: NVFP4Tensor, out_dtype=None, stream=None, out=None):
     if rc != NVFP4_OK:
         raise NVFP4Error(rc, "nvfp4_dequantize")
     return out
-
-
-_GEMM_WORKSPACES = {}
 
 
 def new_gemm_workspace(device):
@@ -276,10 +371,15 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, stream=None, out=None,
     import torch
     if a.cols != b.cols:
         raise ValueError("K mismatch: %d vs %d" % (a.cols, b.cols))
-    out_dtype = out_dtype or torch.bfloat16
     dev = a.codes.device
+    _check_nvfp4("a", a, dev)
+    _check_nvfp4("b", b, dev)
     if out is None:
-        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=dev)
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check_buffer("out", out, (a.rows, b.rows), _out_dtypes(), dev)
+    if split_tail and workspace is not None:
+        _check_workspace(workspace, nvfp4_gemm_workspace_bytes(), dev)
+    _require_gpu(dev)
     od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     oa = Operand(a.codes.data_ptr(), a.scales.data_ptr(), a.global_dec.data_ptr(), a.blocking, 0)
     ob = Operand(b.codes.data_ptr(), b.scales.data_ptr(), b.global_dec.data_ptr(), b.blocking, 0)
@@ -310,6 +410,8 @@ def transpose(x, stream=None, out=None):
     rows, cols = x.shape
     if out is None:
         out = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
+    _check_buffer("out", out, (cols, rows), (torch.bfloat16,), x.device)
+    _require_gpu(x.device)
     rc = nvfp4_transpose_bf16(_ptr(x), rows, cols, x.stride(0), _ptr(out), out.stride(0),
                               _stream(stream, x.device))
     if rc != NVFP4_OK:
@@ -327,6 +429,14 @@ class MXFP4Tensor:
     cols: int
 
 
+def _check_mx(name, q, device=None):
+    import torch
+    device = q.codes.device if device is None else device
+    _check_buffer(name + ".codes", q.codes, (q.rows, q.cols // 2), (torch.uint8,), device, False)
+    _check_buffer(name + ".scales", q.scales, (q.rows, q.cols // 32), (torch.uint8,), device,
+                  False)
+
+
 def mx_quantize(x, stream=None, out=None) -> MXFP4Tensor:
     """Quantize a 2-D bf16 CUDA tensor (row stride x.stride(0)) to MXFP4."""
     import torch
@@ -338,6 +448,11 @@ def mx_quantize(x, stream=None, out=None) -> MXFP4Tensor:
         out = MXFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
                           torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
                           rows, cols)
+    else:
+        if (out.rows, out.cols) != (rows, cols):
+            raise ValueError("out was made for a %dx%d tensor" % (out.rows, out.cols))
+        _check_mx("out", out, dev)
+    _require_gpu(dev)
     rc = mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), _ptr(out.codes), _ptr(out.scales),
                         _stream(stream, dev))
     if rc != NVFP4_OK:
@@ -347,9 +462,12 @@ def mx_quantize(x, stream=None, out=None) -> MXFP4Tensor:
 
 def mx_dequantize(q: MXFP4Tensor, out_dtype=None, stream=None, out=None):
     import torch
-    out_dtype = out_dtype or torch.bfloat16
+    _check_mx("q", q)
     if out is None:
-        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype or torch.bfloat16,
+                          device=q.codes.device)
+    _check_buffer("out", out, (q.rows, q.cols), _out_dtypes(), q.codes.device)
+    _require_gpu(q.codes.device)
     od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     rc = mxfp4_dequantize(_ptr(q.codes), _ptr(q.scales), q.rows, q.cols, _ptr(out),
                           out.stride(0), od, _stream(stream, q.codes.device))
@@ -363,9 +481,13 @@ def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out_dtype=None, stream=None, out=Non
     import torch
     if a.cols != b.cols:
         raise ValueError("K mismatch: %d vs %d" % (a.cols, b.cols))
-    out_dtype = out_dtype or torch.bfloat16
+    dev = a.codes.device
+    _check_mx("a", a, dev)
+    _check_mx("b", b, dev)
     if out is None:
-        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check_buffer("out", out, (a.rows, b.rows), _out_dtypes(), dev)
+    _require_gpu(dev)
     od = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     rc = mxfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), a.rows,
                     b.rows, a.cols, _ptr(out), out.stride(0), od,

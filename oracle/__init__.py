@@ -65,49 +65,56 @@ class _Params(ctypes.Structure):
 _lib = None
 
 
+def declare(L):
+    """Declare the C signatures on a loaded oracle library ``L`` (ctypes.CDLL)."""
+    P = ctypes.c_void_p
+    i64, u64, u8, u16 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint8, ctypes.c_uint16
+    L.orc_e2m1_decode.argtypes = [u8]
+    L.orc_e2m1_decode.restype = ctypes.c_float
+    L.orc_e2m1_encode_rn.argtypes = [ctypes.c_float]
+    L.orc_e2m1_encode_rn.restype = u8
+    L.orc_e2m1_encode_sr.argtypes = [ctypes.c_float, u16]
+    L.orc_e2m1_encode_sr.restype = u8
+    L.orc_e4m3_decode.argtypes = [u8]
+    L.orc_e4m3_decode.restype = ctypes.c_float
+    L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    L.orc_e4m3_encode.restype = u8
+    L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.orc_f32_to_bf16.restype = u16
+    L.orc_f32_to_bf16_array.argtypes = [P, i64, P]
+    L.orc_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(_Params), P, P, P, P]
+    L.orc_quantize.restype = ctypes.c_int
+    L.orc_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int, P]
+    L.orc_dequantize.restype = ctypes.c_int
+    L.orc_dequantize_bf16.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int, P]
+    L.orc_dequantize_bf16.restype = ctypes.c_int
+    L.orc_block_values_f64.argtypes = [P, P, i64, i64, ctypes.c_int, P]
+    L.orc_block_values_f64.restype = ctypes.c_int
+    L.orc_e4m3_encode_array.argtypes = [P, i64, P]
+    L.orc_e2m1_encode_rn_array.argtypes = [P, i64, P]
+    L.orc_e2m1_encode_sr_array.argtypes = [P, P, i64, P]
+    L.orc_philox_array.argtypes = [P, P, i64, P]
+    L.orc_sr_bits_array.argtypes = [u64, u64, i64, P]
+    L.orc_rht16_rows.argtypes = [P, i64, u64, P]
+    L.orc_rht_signs.argtypes = [u64, P]
+    L.orc_rht16_rows_signs.argtypes = [P, i64, P, P]
+    L.orc_abi_version.restype = ctypes.c_int
+    L.orc_mx_scale.argtypes = [ctypes.c_float]
+    L.orc_mx_scale.restype = ctypes.c_uint8
+    L.orc_mx_quantize.argtypes = [P, i64, i64, i64, P, P, P]
+    L.orc_mx_quantize.restype = ctypes.c_int
+    L.orc_mx_block_values_f64.argtypes = [P, P, i64, i64, P]
+    L.orc_mx_block_values_f64.restype = ctypes.c_int
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH) or (
                 os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        i64, u64, u8, u16 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint8, ctypes.c_uint16
-        L.orc_e2m1_decode.argtypes = [u8]
-        L.orc_e2m1_decode.restype = ctypes.c_float
-        L.orc_e2m1_encode_rn.argtypes = [ctypes.c_float]
-        L.orc_e2m1_encode_rn.restype = u8
-        L.orc_e2m1_encode_sr.argtypes = [ctypes.c_float, u16]
-        L.orc_e2m1_encode_sr.restype = u8
-        L.orc_e4m3_decode.argtypes = [u8]
-        L.orc_e4m3_decode.restype = ctypes.c_float
-        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
-        L.orc_e4m3_encode.restype = u8
-        L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
-        L.orc_f32_to_bf16.restype = u16
-        L.orc_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(_Params), P, P, P, P]
-        L.orc_quantize.restype = ctypes.c_int
-        L.orc_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int, P]
-        L.orc_dequantize.restype = ctypes.c_int
-        L.orc_block_values_f64.argtypes = [P, P, i64, i64, ctypes.c_int, P]
-        L.orc_block_values_f64.restype = ctypes.c_int
-        L.orc_e4m3_encode_array.argtypes = [P, i64, P]
-        L.orc_e2m1_encode_rn_array.argtypes = [P, i64, P]
-        L.orc_e2m1_encode_sr_array.argtypes = [P, P, i64, P]
-        L.orc_philox_array.argtypes = [P, P, i64, P]
-        L.orc_sr_bits_array.argtypes = [u64, u64, i64, P]
-        L.orc_rht16_rows.argtypes = [P, i64, u64, P]
-        L.orc_rht_signs.argtypes = [u64, P]
-        L.orc_rht16_rows_signs.argtypes = [P, i64, P, P]
-        L.orc_abi_version.restype = ctypes.c_int
-        L.orc_mx_scale.argtypes = [ctypes.c_float]
-        L.orc_mx_scale.restype = ctypes.c_uint8
-        L.orc_mx_quantize.argtypes = [P, i64, i64, i64, P, P, P]
-        L.orc_mx_quantize.restype = ctypes.c_int
-        L.orc_mx_block_values_f64.argtypes = [P, P, i64, i64, P]
-        L.orc_mx_block_values_f64.restype = ctypes.c_int
-        _lib = L
+        _lib = declare(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
@@ -191,10 +198,12 @@ def rht16_with_signs(x: np.ndarray, d: np.ndarray) -> np.ndarray:
     return y
 
 
-def f32_to_bf16(f: np.ndarray) -> np.ndarray:
-    L = lib()
-    f = np.asarray(f, dtype=np.float32).ravel()
-    return np.array([L.orc_f32_to_bf16(float(v)) for v in f], dtype=np.uint16)
+def f32_to_bf16(f: np.ndarray, L=None) -> np.ndarray:
+    """bf16 bit patterns of binary32 values, nearest-even (``orc_f32_to_bf16``)."""
+    f = np.ascontiguousarray(f, dtype=np.float32).ravel()
+    out = np.empty(f.shape, dtype=np.uint16)
+    (L or lib()).orc_f32_to_bf16_array(_p(f), f.size, _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- quantize
@@ -227,27 +236,29 @@ def quantize(x_bf16: np.ndarray, *, blocking: int = BLOCK_1x16, rounding: int = 
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, global_dec, rows: int, cols: int,
-               blocking: int = BLOCK_1x16) -> np.ndarray:
+               blocking: int = BLOCK_1x16, L=None) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     y = np.empty((rows, cols), dtype=np.float32)
-    rc = lib().orc_dequantize(_p(codes), _p(scales), float(np.float32(global_dec)), rows,
+    rc = (L or lib()).orc_dequantize(_p(codes), _p(scales), float(np.float32(global_dec)), rows,
                               cols, blocking, _p(y))
     if rc != 0:
         raise QuantizeError("bad shape")
     return y
 
 
-def dequantize_bf16(codes, scales, global_dec, rows, cols, blocking=BLOCK_1x16):
-    """Dequantize to bf16 (uint16 bit patterns): round-to-nearest-even of the fp32 value."""
-    y = dequantize(codes, scales, global_dec, rows, cols, blocking)
-    u = y.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    out = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = np.isnan(y)
-    if nan.any():
-        out[nan] = ((y.view(np.uint32)[nan] >> 16) | 0x40).astype(np.uint16)
-    return out
+def dequantize_bf16(codes, scales, global_dec, rows, cols, blocking=BLOCK_1x16, L=None):
+    """Dequantize to bf16 (uint16 bit patterns): each binary32 value of ``dequantize``
+    rounded to nearest-even by the oracle's one bf16 conversion, ``orc_f32_to_bf16``.
+    ``L``: another build of the oracle library (tests load planted variants)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    y = np.empty((rows, cols), dtype=np.uint16)
+    rc = (L or lib()).orc_dequantize_bf16(_p(codes), _p(scales), float(np.float32(global_dec)),
+                                          rows, cols, blocking, _p(y))
+    if rc != 0:
+        raise QuantizeError("bad shape")
+    return y
 
 
 def block_values_f64(codes, scales, rows, cols, blocking=BLOCK_1x16) -> np.ndarray:
@@ -317,6 +328,27 @@ def gemm_reference(a, b, row_slice=None) -> np.ndarray:
     c = np.matmul(qa, qb.T)
     c *= float(np.float32(ga)) * float(np.float32(gb))
     return c
+
+
+def gemm_reference_chunks(a, b, chunk, with_abs=False):
+    """``gemm_reference`` in row chunks: yields (r0, r1, C[r0:r1]) and, with ``with_abs``,
+    also s_A s_B |A_deq| |B_deq|^T for those rows (the scale of the fp32 summation error).
+    The block values are formed once; each chunk is one binary64 matmul (BLAS dgemm)."""
+    ca, sa, ga, ma, ka, bla = a
+    cb, sb, gb, nb, kb, blb = b
+    assert ka == kb
+    qa = block_values_f64(ca, sa, ma, ka, bla)
+    qbt = np.ascontiguousarray(block_values_f64(cb, sb, nb, kb, blb).T)
+    absbt = np.abs(qbt) if with_abs else None
+    g = float(np.float32(ga)) * float(np.float32(gb))
+    for r0 in range(0, ma, chunk):
+        r1 = min(ma, r0 + chunk)
+        c = np.matmul(qa[r0:r1], qbt)
+        c *= g
+        if with_abs:
+            yield r0, r1, c, np.matmul(np.abs(qa[r0:r1]), absbt) * abs(g)
+        else:
+            yield r0, r1, c
 
 
 # ------------------------------------------------------------------ linear layer

@@ -402,6 +402,28 @@ int orc_dequantize(const uint8_t *codes, const uint8_t *scales, float global_dec
     return 0;
 }
 
+/* The same values as orc_dequantize, each rounded to bfloat16 by orc_f32_to_bf16 (nearest,
+ * ties to even).  READING: the pages name no output precision of the dequantized tensor;
+ * bf16 output rounds the binary32 value once, the usual conversion of that format. */
+int orc_dequantize_bf16(const uint8_t *codes, const uint8_t *scales, float global_dec,
+                        int64_t rows, int64_t cols, int blocking, uint16_t *y)
+{
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16)
+        return -1;
+    int64_t bh = (blocking == ORC_BLOCK_16x16) ? 16 : 1;
+    int64_t nbc = cols / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = codes[r * (cols / 2) + c / 2];
+            uint8_t q = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15u);
+            float sbd = orc_e4m3_decode(scales[(r / bh) * nbc + c / 16]);
+            float e = orc_e2m1_decode(q) * sbd;
+            y[r * cols + c] = orc_f32_to_bf16(e * global_dec);
+        }
+    return 0;
+}
+
 /* Exact block-scaled values e2m1(q) * sbd (no tensor scale), in binary64: the GEMM
  * reference multiplies these and applies both tensor scales afterwards. */
 int orc_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
@@ -435,6 +457,13 @@ uint16_t orc_f32_to_bf16(float f)
 /* ------------------------------------------------------------------------- */
 /* Array helpers for the tests                                                */
 /* ------------------------------------------------------------------------- */
+
+void orc_f32_to_bf16_array(const float *f, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_bf16(f[i]);
+}
 
 void orc_e4m3_encode_array(const float *s, int64_t n, uint8_t *out)
 {

@@ -47,6 +47,8 @@ int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                  uint32_t *status);
 int orc_dequantize(const uint8_t *codes, const uint8_t *scales, float global_dec,
                    int64_t rows, int64_t cols, int blocking, float *y);
+int orc_dequantize_bf16(const uint8_t *codes, const uint8_t *scales, float global_dec,
+                        int64_t rows, int64_t cols, int blocking, uint16_t *y);
 int orc_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                          int64_t cols, int blocking, double *out);
 
@@ -58,6 +60,7 @@ int orc_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
 int orc_mx_block_values_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                             int64_t cols, double *out);
 
+void orc_f32_to_bf16_array(const float *f, int64_t n, uint16_t *out);
 void orc_e4m3_encode_array(const float *s, int64_t n, uint8_t *out);
 void orc_e2m1_encode_rn_array(const float *v, int64_t n, uint8_t *out);
 void orc_e2m1_encode_sr_array(const float *v, const uint16_t *k, int64_t n, uint8_t *out);

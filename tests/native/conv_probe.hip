@@ -1,0 +1,136 @@
+// conv_probe.hip -- test-only kernels that run the library's device conversion helpers
+// (block_scaled_fp4_06_amd/csrc/nvfp4_device.hpp) over large sets of inputs, so that the
+// GPU tests can compare them with the CPU oracle's codecs value by value.
+//
+// The quantizers and the GEMM rely on these hardware conversions being exactly the
+// rounding the pages' format needs (E4M3 block scales and E2M1 elements, [NV-blog]
+// recipe section bullets 1-2; [PR] "MVFP4格式的核心架构革新"):
+//   e4m3_encode       clamp at 448, then the fp8 conversion: nearest-even E4M3FN code;
+//   e4m3_decode       fp8 -> fp32;  e4m3_pair_f16: fp8 -> fp16 (the GEMM's block scales);
+//   e2m1_rn_pack16    the scaled fp4 conversion with scale 1.0: nearest-even E2M1 codes;
+//   e2m1_decode_pair  fp4 -> fp32;  dequant8_f16: fp4 -> fp16 times the block scale;
+//   bf16_bits_rn      fp32 -> bf16 nearest-even (the GEMM epilogues).
+// Inputs are generated on the device from binary32 bit patterns first + i * stride
+// (modulo 2^32); every entry point launches on the caller's stream and returns the HIP
+// status of the launch.  Grids are grid-stride loops over exactly n items.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_device.hpp"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+unsigned grid_for(uint64_t n) {
+  const uint64_t g = (n + kThreads - 1) / kThreads;
+  return (unsigned)(g < 16384 ? (g ? g : 1) : 16384);
+}
+
+__device__ __forceinline__ float pattern(uint32_t first, uint32_t stride, uint64_t i) {
+  return __uint_as_float(first + (uint32_t)i * stride);
+}
+
+__global__ void e4m3_encode_kernel(uint32_t first, uint32_t stride, uint64_t n, uint8_t *out) {
+  for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * kThreads)
+    out[i] = (uint8_t)nvfp4::e4m3_encode(pattern(first, stride, i));
+}
+
+// n16 groups of 16 consecutive patterns, each packed to 8 bytes of codes (multiplier 1.0)
+__global__ void e2m1_encode_kernel(uint32_t first, uint32_t stride, uint64_t n16, uint2 *out) {
+  for (uint64_t g = blockIdx.x * (uint64_t)kThreads + threadIdx.x; g < n16;
+       g += (uint64_t)gridDim.x * kThreads) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = pattern(first, stride, 16 * g + j);
+    out[g] = nvfp4::e2m1_rn_pack16(v, 1.0f);
+  }
+}
+
+__global__ void bf16_kernel(uint32_t first, uint32_t stride, uint64_t n, uint16_t *out) {
+  for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * kThreads)
+    out[i] = nvfp4::bf16_bits_rn(pattern(first, stride, i));
+}
+
+// Small tables, one thread per entry:
+//   e4m3_dec[c]          e4m3_decode(c) for every byte c                     (256 floats)
+//   e2m1_dec[2 t + h]    e2m1_decode_pair of byte t: h = 0 the low nibble, 1 the high one
+//                        (512 floats); the byte in positions 1-3 must decode alike
+//                        (else bit 0 of *mismatch)
+//   scale_pairs[2 p + h] e4m3_pair_f16 of the byte pair p = b1 << 8 | b0: h = 0 -> b0,
+//                        1 -> b1 (65536 x 2 fp16); the pair in the upper half of the word
+//                        must decode alike (else bit 1)
+//   dequant[16 s + c]    element 0 of dequant8_f16(code c in all eight positions, scale =
+//                        e4m3 byte s as fp16) (4096 fp16); the other seven must equal it
+//                        (else bit 2)
+__global__ void tables_kernel(float *e4m3_dec, float *e2m1_dec, uint16_t *scale_pairs,
+                              uint16_t *dequant, uint32_t *mismatch) {
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  if (t < 256u) e4m3_dec[t] = nvfp4::e4m3_decode(t);
+  if (t < 256u) {
+    // byte position b (0..3) holding the code pair (lo = t & 15, hi = t >> 4)
+    const uint32_t byte = t & 0xFFu;
+    const nvfp4::float2_t p0 = nvfp4::e2m1_decode_pair<0>(byte);
+    const nvfp4::float2_t p1 = nvfp4::e2m1_decode_pair<1>(byte << 8);
+    const nvfp4::float2_t p2 = nvfp4::e2m1_decode_pair<2>(byte << 16);
+    const nvfp4::float2_t p3 = nvfp4::e2m1_decode_pair<3>(byte << 24);
+    // every position must decode alike; store position 0 and flag differences
+    e2m1_dec[2 * t] = p0[0];
+    e2m1_dec[2 * t + 1] = p0[1];
+    if (__float_as_uint(p1[0]) != __float_as_uint(p0[0]) || __float_as_uint(p1[1]) != __float_as_uint(p0[1]) ||
+        __float_as_uint(p2[0]) != __float_as_uint(p0[0]) || __float_as_uint(p2[1]) != __float_as_uint(p0[1]) ||
+        __float_as_uint(p3[0]) != __float_as_uint(p0[0]) || __float_as_uint(p3[1]) != __float_as_uint(p0[1]))
+      atomicOr(mismatch, 1u);
+  }
+  if (t < 65536u) {
+    const nvfp4::half2_t lo = nvfp4::e4m3_pair_f16(t, 0);
+    const nvfp4::half2_t hi = nvfp4::e4m3_pair_f16(t << 16, 1);
+    scale_pairs[2 * t] = __builtin_bit_cast(uint16_t, lo.x);
+    scale_pairs[2 * t + 1] = __builtin_bit_cast(uint16_t, lo.y);
+    if (__builtin_bit_cast(uint16_t, hi.x) != __builtin_bit_cast(uint16_t, lo.x) ||
+        __builtin_bit_cast(uint16_t, hi.y) != __builtin_bit_cast(uint16_t, lo.y))
+      atomicOr(mismatch, 2u);
+  }
+  if (t < 4096u) {
+    const uint32_t s = t >> 4, c = t & 15u;
+    const _Float16 sbd = nvfp4::e4m3_pair_f16(s, 0).x;
+    const uint32_t w = c * 0x11111111u;   // the code in all eight positions
+    const nvfp4::half8_t d = nvfp4::dequant8_f16(w, sbd);
+    const uint16_t d0 = __builtin_bit_cast(uint16_t, d[0]);
+    dequant[t] = d0;
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+      if (__builtin_bit_cast(uint16_t, d[j]) != d0) atomicOr(mismatch, 4u);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int probe_e4m3_encode(uint32_t first, uint32_t stride, uint64_t n, uint8_t *out, hipStream_t s) {
+  e4m3_encode_kernel<<<grid_for(n), kThreads, 0, s>>>(first, stride, n, out);
+  return (int)hipGetLastError();
+}
+
+int probe_e2m1_encode(uint32_t first, uint32_t stride, uint64_t n16, uint8_t *out, hipStream_t s) {
+  e2m1_encode_kernel<<<grid_for(n16), kThreads, 0, s>>>(first, stride, n16,
+                                                        reinterpret_cast<uint2 *>(out));
+  return (int)hipGetLastError();
+}
+
+int probe_bf16(uint32_t first, uint32_t stride, uint64_t n, uint16_t *out, hipStream_t s) {
+  bf16_kernel<<<grid_for(n), kThreads, 0, s>>>(first, stride, n, out);
+  return (int)hipGetLastError();
+}
+
+int probe_tables(float *e4m3_dec, float *e2m1_dec, uint16_t *scale_pairs, uint16_t *dequant,
+                 uint32_t *mismatch, hipStream_t s) {
+  tables_kernel<<<65536 / kThreads, kThreads, 0, s>>>(e4m3_dec, e2m1_dec, scale_pairs, dequant,
+                                                      mismatch);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -203,6 +203,52 @@ def test_transpose_argument_errors(lib):
     assert t(rows=0, x=None, y=None) == ERR["OK"]
 
 
+# Shapes whose element count overflows a 64-bit product (2^68), wraps to zero (2^64) or
+# wraps to exactly 2^35 ((2^33 + 16) * 2^31 = 2^64 + 2^35), and one just above 2^35.
+HUGE = [(1 << 34, 1 << 34), (1 << 32, 1 << 32), ((1 << 33) + 16, 1 << 31), ((1 << 35) + 16, 1 << 4),
+        (1 << 20, (1 << 15) + 16)]
+
+
+@pytest.mark.parametrize("rows,cols", HUGE)
+def test_huge_shapes_rejected_without_overflow(lib, rows, cols):
+    P = N.QuantParams
+    for prm in (P(0, 0, 0, 0, 0, 0, 0), P(0, 1, 0, 0, 0, 0, 0), P(0, 0, 1, 0, 0, 0, 0),
+                P(1, 0, 0, 0, 0, 0, 0), P(1, 1, 1, 0, 0, 0, 0)):
+        assert q(prm, rows=rows, cols=cols, ld=cols) == ERR["SHAPE"], (rows, cols, prm.blocking)
+    assert q(P(1, 0, 0, 0, 0, 0, 0), rows=rows, cols=cols, ld=cols, ct=FAKE,
+             st=FAKE) == ERR["SHAPE"]
+    for blk in (0, 1):
+        for od in (0, 1):
+            assert N.nvfp4_dequantize(FAKE, FAKE, FAKE, rows, cols, blk, FAKE, cols, od,
+                                      None) == ERR["SHAPE"]
+    mcols = cols - (cols & 31)   # MXFP4 blocks are 32 elements
+    if mcols:
+        assert N.mxfp4_quantize(FAKE, rows, mcols, mcols, FAKE, FAKE, None) == ERR["SHAPE"]
+        assert N.mxfp4_dequantize(FAKE, FAKE, rows, mcols, FAKE, mcols, 0, None) == ERR["SHAPE"]
+    assert N.nvfp4_transpose_bf16(FAKE, rows, cols, cols, FAKE, rows, None) == ERR["SHAPE"]
+
+
+def test_leading_dimension_overflow_rejected(lib):
+    # a small tensor whose row stride makes (rows - 1) * ld overflow 64-bit offsets
+    big = 1 << 62
+    assert q(rows=32, cols=32, ld=big) == ERR["SHAPE"]
+    assert N.nvfp4_dequantize(FAKE, FAKE, FAKE, 32, 32, 0, FAKE, big, 0, None) == ERR["SHAPE"]
+    assert N.mxfp4_quantize(FAKE, 32, 64, big, FAKE, FAKE, None) == ERR["SHAPE"]
+    assert N.mxfp4_dequantize(FAKE, FAKE, 32, 64, FAKE, big, 0, None) == ERR["SHAPE"]
+    assert N.nvfp4_transpose_bf16(FAKE, 32, 64, big, FAKE, 32, None) == ERR["SHAPE"]
+    assert N.nvfp4_transpose_bf16(FAKE, 32, 64, 64, FAKE, big, None) == ERR["SHAPE"]
+    op = N.Operand(FAKE, FAKE, FAKE, 0, 0)
+    assert N.nvfp4_gemm(op, op, 32, 32, 64, FAKE, big, 0, None) == ERR["SHAPE"]
+    assert N.mxfp4_gemm(FAKE, FAKE, FAKE, FAKE, 32, 32, 64, FAKE, big, 0, None) == ERR["SHAPE"]
+    # a stride just below the largest whose span (rows - 1) * ld + cols stays within 2^60
+    # elements passes the shape checks (and then fails on alignment); the next multiple of 8
+    # above the largest does not
+    ld_max = ((1 << 60) - 16) // 15
+    assert ld_max % 8 == 0
+    assert q(rows=16, cols=16, ld=ld_max - 1) == ERR["ALIGN"]
+    assert q(rows=16, cols=16, ld=ld_max + 8) == ERR["SHAPE"]
+
+
 def test_python_wrapper_raises_when_library_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(N, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):

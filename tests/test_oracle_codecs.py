@@ -189,3 +189,67 @@ def test_bf16_rounding_matches_torch(orc):
     assert np.array_equal(orc.f32_to_bf16(x), ref)
     y = orc.dequantize_bf16(np.zeros((16, 8), np.uint8), np.zeros((16, 1), np.uint8), 1.0, 16, 16)
     assert np.all(y == 0)
+
+
+def _bf16_dequant_cases():
+    """Codes 0..15 in every row, one E4M3 scale byte per row (all 256: zero, subnormals,
+    both signs, 448, the NaN bytes), times tensor scales chosen so that the binary32 values
+    land on bf16 ties (1 + 2^-8 goes down to even, 1 + 3 * 2^-8 up), next to them, in the
+    binary32 subnormal range, at the top of the range (rounding to inf), on inf and NaN,
+    and at random over 2^-140 .. 2^120."""
+    codes = np.tile(np.array([(2 * j + 1) << 4 | (2 * j) for j in range(8)], np.uint8), (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    bits = [0x3F800000, 0x3F808000, 0x3F818000, 0x3F804000, 0x3F80C000, 0x3F7F8000,
+            0x3FFF8000, 0x00018000, 0x00008000, 0x00000001, 0x00800000, 0x0B808000,
+            0x7F7FFFFF, 0x7F7F8000, 0x7F000000, 0x7F800000, 0x7FC00000, 0x00000000,
+            0x80000000, 0xBF808000]
+    rng = np.random.default_rng(11)
+    rnd = (rng.integers(-140, 120, 300).astype(np.float64) +
+           rng.uniform(0, 1, 300)).astype(np.float64)
+    r32 = np.exp2(rnd).astype(np.float32).view(np.uint32)
+    r32 = np.concatenate([r32, (r32 & 0xFFFF0000) | 0x8000])   # and their tie patterns
+    g = np.concatenate([np.array(bits, np.uint32), r32]).view(np.float32)
+    return codes, scales, g
+
+
+def bf16_dequant_mismatches(orc, L=None):
+    """Elements where the oracle's bf16 dequantize differs from torch's binary32 -> bf16
+    cast of the oracle's binary32 dequantize (NaN must stay NaN; its payload is free)."""
+    codes, scales, gs = _bf16_dequant_cases()
+    bad = ties = 0
+    for g in gs:
+        y32 = orc.dequantize(codes, scales, g, 256, 16, L=L)
+        got = orc.dequantize_bf16(codes, scales, g, 256, 16, L=L)
+        ref = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(y32)
+        got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        bad += int(np.count_nonzero(nan != got_nan))
+        bad += int(np.count_nonzero((got != ref) & ~nan))
+        ties += int(np.count_nonzero((y32.view(np.uint32) & 0xFFFF) == 0x8000))
+    return bad, ties
+
+
+def test_dequantize_bf16_matches_torch_cast(orc):
+    """The bf16 dequantize ([PR] "MVFP4与MXFP4": code value times block scale; FP32 tensor
+    scale on top, "MVFP4格式的核心架构革新") equals torch's nearest-even cast of the binary32
+    dequantize on every case, ties included."""
+    bad, ties = bf16_dequant_mismatches(orc)
+    assert bad == 0
+    assert ties > 10000   # the cases do exercise the tie rule
+
+
+def test_dequantize_bf16_pin_catches_round_half_up(orc, tmp_path):
+    """Plant round-half-up in a copy of the oracle's bf16 conversion: the pin above fails."""
+    import ctypes
+    import subprocess
+    src = open(os.path.join(os.path.dirname(orc.__file__), "nvfp4_oracle.c")).read()
+    rne = "return (uint16_t)((u + 0x7FFFu + lsb) >> 16);"
+    assert src.count(rne) == 1
+    (tmp_path / "planted.c").write_text(src.replace(rne, "(void)lsb; return (uint16_t)((u + 0x8000u) >> 16);"))
+    so = str(tmp_path / "planted.so")
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                           "-shared", "-I", os.path.dirname(orc.__file__), "-o", so,
+                           str(tmp_path / "planted.c"), "-lm"])
+    planted = orc.declare(ctypes.CDLL(so))
+    bad, _ = bf16_dequant_mismatches(orc, L=planted)
+    assert bad > 0

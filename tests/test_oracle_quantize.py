@@ -281,3 +281,19 @@ def test_gemm_reference_exact_bruteforce(orc):
                 s += fa * fb
             exact = s * Fraction(float(qa[2])) * Fraction(float(qb[2]))
             assert abs(Fraction(c[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+
+
+def test_gemm_reference_chunks_equal_whole(orc):
+    """The row-chunked reference (used at workload-5 size) is the same product, and its
+    |A||B| scale bounds every |C| element."""
+    rng = np.random.default_rng(9)
+    a = W.f32_to_bf16_bits(rng.standard_normal((80, 64), dtype=np.float32))
+    b = W.f32_to_bf16_bits(rng.standard_normal((48, 64), dtype=np.float32))
+    qa = orc.quantize(a, rht=True, rht_seed=5)
+    qb = orc.quantize(b, blocking=orc.BLOCK_16x16)
+    ta, tb = (qa[0], qa[1], qa[2], 80, 64, 0), (qb[0], qb[1], qb[2], 48, 64, 1)
+    whole = orc.gemm_reference(ta, tb)
+    parts = list(orc.gemm_reference_chunks(ta, tb, 32, with_abs=True))
+    assert [(r0, r1) for r0, r1, _, _ in parts] == [(0, 32), (32, 64), (64, 80)]
+    assert np.array_equal(np.concatenate([c for _, _, c, _ in parts]), whole)
+    assert all(np.all(np.abs(c) <= ab * (1 + 1e-12)) for _, _, c, ab in parts)
