@@ -46,7 +46,7 @@ class NVFP4Error(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, nvfp4_status_string(status), status))
 
 
-EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
+EXPORTED = ("nvfp4_quantize_workspace_bytes", "nvfp4_quantize", "nvfp4_quantize_noalloc",
             "nvfp4_dequantize",
             "nvfp4_gemm", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_transpose_bf16", "mxfp4_quantize", "mxfp4_dequantize",
             "mxfp4_gemm",
@@ -70,6 +70,9 @@ def load(path: str = LIB_PATH):
     L.nvfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(QuantParams), P, P, P, P, P,
                                  P, P, ctypes.c_size_t, P]
     L.nvfp4_quantize.restype = ctypes.c_int
+    L.nvfp4_quantize_noalloc.argtypes = [P, i64, i64, i64, ctypes.POINTER(QuantParams), P, P,
+                                         P, P, P, P, P]
+    L.nvfp4_quantize_noalloc.restype = ctypes.c_int
     L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, i64, i32, P]
     L.nvfp4_dequantize.restype = ctypes.c_int
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64,
@@ -106,6 +109,13 @@ def nvfp4_quantize(x, rows, cols, ld_x, params: QuantParams, codes, scales, glob
     return int(load().nvfp4_quantize(x, rows, cols, ld_x, ctypes.byref(params), codes, scales,
                                      global_dec, codes_t, scales_t, dev_status, workspace,
                                      workspace_bytes, stream))
+
+
+def nvfp4_quantize_noalloc(x, rows, cols, ld_x, params: QuantParams, codes, scales,
+                           global_dec, codes_t, scales_t, dev_status, stream) -> int:
+    return int(load().nvfp4_quantize_noalloc(x, rows, cols, ld_x, ctypes.byref(params), codes,
+                                             scales, global_dec, codes_t, scales_t, dev_status,
+                                             stream))
 
 
 def nvfp4_dequantize(codes, scales, global_dec, rows, cols, blocking, y, ld_y, out_dtype,

@@ -133,6 +133,26 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
                             nvfp4_stream_t stream);
 
 /*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The library keeps the workspace in a file-scope device
+ * array of nvfp4_quantize_workspace_bytes() bytes (8 MiB + 8 KiB), one per GPU, held until
+ * the process ends; it covers every shape the ABI accepts.  The call allocates nothing.
+ *
+ * Arguments, results and errors as nvfp4_quantize, without workspace/workspace_bytes.  The
+ * array is found on the device of `stream`; its address is looked up once per device (the
+ * first call on a device makes that HIP call; a failure returns NVFP4_ERR_HIP).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (several streams or host threads) race and must not be made; calls in stream order,
+ * graph replays included, are fine.
+ */
+nvfp4_status nvfp4_quantize_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                    int64_t ld_x, const nvfp4_quant_params *p, uint8_t *codes,
+                                    uint8_t *scales, float *global_dec, uint8_t *codes_t,
+                                    uint8_t *scales_t, uint32_t *dev_status,
+                                    nvfp4_stream_t stream);
+
+/*
  * nvfp4_dequantize -- y = e2m1(code) * e4m3(scale) * global ([PR] "MVFP4与MXFP4": a 4-bit
  * value times its block scale gives the real value; "MVFP4格式的核心架构革新": the FP32
  * tensor scale on top).  The first product is exact; bf16 output rounds the fp32 value
