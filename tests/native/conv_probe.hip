@@ -59,14 +59,16 @@ __global__ void bf16_kernel(uint32_t first, uint32_t stride, uint64_t n, uint16_
 //   e2m1_dec[2 t + h]    e2m1_decode_pair of byte t: h = 0 the low nibble, 1 the high one
 //                        (512 floats); the byte in positions 1-3 must decode alike
 //                        (else bit 0 of *mismatch)
-//   scale_pairs[2 p + h] e4m3_pair_f16 of the byte pair p = b1 << 8 | b0: h = 0 -> b0,
-//                        1 -> b1 (65536 x 2 fp16); the pair in the upper half of the word
-//                        must decode alike (else bit 1)
-//   dequant[16 s + c]    element 0 of dequant8_f16(code c in all eight positions, scale =
-//                        e4m3 byte s as fp16) (4096 fp16); the other seven must equal it
-//                        (else bit 2)
-__global__ void tables_kernel(float *e4m3_dec, float *e2m1_dec, uint16_t *scale_pairs,
-                              uint16_t *dequant, uint32_t *mismatch) {
+//   scale_pairs[p]       e4m3_pair_f16 of the byte pair p = b1 << 8 | b0, as the packed
+//                        register (low fp16 = b0, high = b1; 65536 dwords); the pair in the
+//                        upper half of the word must decode alike (else bit 1)
+//   dequant[8 (16 s + c) + j]  element j of dequant8_f16(code c in all eight positions,
+//                        scale = e4m3 byte s as fp16), stored as the four packed registers
+//                        (4096 x 8 fp16)
+// Results are stored as whole packed registers: this compiler stores the low half of the
+// register for an fp16 element taken out of a packed conversion result on its own.
+__global__ void tables_kernel(float *e4m3_dec, float *e2m1_dec, uint32_t *scale_pairs,
+                              uint4 *dequant, uint32_t *mismatch) {
   const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
   if (t < 256u) e4m3_dec[t] = nvfp4::e4m3_decode(t);
   if (t < 256u) {
@@ -85,24 +87,16 @@ __global__ void tables_kernel(float *e4m3_dec, float *e2m1_dec, uint16_t *scale_
       atomicOr(mismatch, 1u);
   }
   if (t < 65536u) {
-    const nvfp4::half2_t lo = nvfp4::e4m3_pair_f16(t, 0);
-    const nvfp4::half2_t hi = nvfp4::e4m3_pair_f16(t << 16, 1);
-    scale_pairs[2 * t] = __builtin_bit_cast(uint16_t, lo.x);
-    scale_pairs[2 * t + 1] = __builtin_bit_cast(uint16_t, lo.y);
-    if (__builtin_bit_cast(uint16_t, hi.x) != __builtin_bit_cast(uint16_t, lo.x) ||
-        __builtin_bit_cast(uint16_t, hi.y) != __builtin_bit_cast(uint16_t, lo.y))
-      atomicOr(mismatch, 2u);
+    const uint32_t lo = __builtin_bit_cast(uint32_t, nvfp4::e4m3_pair_f16(t, 0));
+    const uint32_t hi = __builtin_bit_cast(uint32_t, nvfp4::e4m3_pair_f16(t << 16, 1));
+    scale_pairs[t] = lo;
+    if (hi != lo) atomicOr(mismatch, 2u);
   }
   if (t < 4096u) {
     const uint32_t s = t >> 4, c = t & 15u;
     const _Float16 sbd = nvfp4::e4m3_pair_f16(s, 0).x;
     const uint32_t w = c * 0x11111111u;   // the code in all eight positions
-    const nvfp4::half8_t d = nvfp4::dequant8_f16(w, sbd);
-    const uint16_t d0 = __builtin_bit_cast(uint16_t, d[0]);
-    dequant[t] = d0;
-#pragma unroll
-    for (int j = 1; j < 8; ++j)
-      if (__builtin_bit_cast(uint16_t, d[j]) != d0) atomicOr(mismatch, 4u);
+    dequant[t] = __builtin_bit_cast(uint4, nvfp4::dequant8_f16(w, sbd));
   }
 }
 
@@ -126,7 +120,7 @@ int probe_bf16(uint32_t first, uint32_t stride, uint64_t n, uint16_t *out, hipSt
   return (int)hipGetLastError();
 }
 
-int probe_tables(float *e4m3_dec, float *e2m1_dec, uint16_t *scale_pairs, uint16_t *dequant,
+int probe_tables(float *e4m3_dec, float *e2m1_dec, uint32_t *scale_pairs, uint4 *dequant,
                  uint32_t *mismatch, hipStream_t s) {
   tables_kernel<<<65536 / kThreads, kThreads, 0, s>>>(e4m3_dec, e2m1_dec, scale_pairs, dequant,
                                                       mismatch);

@@ -135,8 +135,8 @@ def test_bf16_conversion_matches_oracle_on_every_binary32(probe):
 def test_decoders_match_oracle(probe):
     e4 = torch.empty(256, dtype=torch.float32, device="cuda")
     e2 = torch.empty(512, dtype=torch.float32, device="cuda")
-    sp = torch.empty(131072, dtype=torch.int16, device="cuda")
-    dq = torch.empty(4096, dtype=torch.int16, device="cuda")
+    sp = torch.empty(65536, dtype=torch.int32, device="cuda")      # packed fp16 pairs
+    dq = torch.empty(4096 * 8, dtype=torch.int16, device="cuda")   # 8 fp16 per (scale, code)
     mm = torch.zeros(1, dtype=torch.int32, device="cuda")
     assert probe.probe_tables(*(ctypes.c_void_p(t.data_ptr()) for t in (e4, e2, sp, dq, mm)),
                               _stream()) == 0
@@ -151,8 +151,10 @@ def test_decoders_match_oracle(probe):
     # fp4 pairs: byte t -> (code t & 15, code t >> 4)
     ref2 = oracle.e2m1_decode(np.stack([codes & 15, codes >> 4], 1).ravel())
     assert np.array_equal(e2.cpu().numpy().view(np.uint32), ref2.view(np.uint32))
-    # E4M3 byte pairs as fp16: byte b0 of pair p in slot 0, b1 in slot 1
-    got_sp = sp.cpu().numpy().view(np.float16).astype(np.float64).reshape(65536, 2)
+    # E4M3 byte pairs as fp16: byte b0 of pair p in the low half, b1 in the high half
+    got_sp = sp.cpu().numpy().view(np.uint32)
+    got_sp = np.stack([got_sp & 0xFFFF, got_sp >> 16], 1).astype(np.uint16).view(
+        np.float16).astype(np.float64)
     p = np.arange(65536)
     for h, b in ((0, p & 0xFF), (1, p >> 8)):
         ref = oracle.e4m3_decode(b.astype(np.uint8)).astype(np.float64)
@@ -162,9 +164,11 @@ def test_decoders_match_oracle(probe):
         # signed zeros keep their sign
         assert np.array_equal(np.signbit(got_sp[~nan, h]), np.signbit(ref[~nan]))
     # the GEMM's operand values: e2m1(c) * e4m3(s) in fp16, exact for every finite scale
-    got_dq = dq.cpu().numpy().view(np.float16).astype(np.float64).reshape(256, 16)
+    # (all eight positions of the dword hold the same code, so all eight values agree)
+    got_dq = dq.cpu().numpy().view(np.float16).astype(np.float64).reshape(256, 16, 8)
     ref_dq = (oracle.e4m3_decode(codes).astype(np.float64)[:, None] *
               oracle.e2m1_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)[None, :])
+    ref_dq = np.repeat(ref_dq[:, :, None], 8, axis=2)
     nan = np.isnan(ref_dq)
     assert np.array_equal(np.isnan(got_dq), nan)
     assert np.array_equal(got_dq[~nan], ref_dq[~nan])
