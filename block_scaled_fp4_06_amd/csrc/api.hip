@@ -113,7 +113,7 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
   if (st != NVFP4_OK) return st;
   if (!workspace || workspace_bytes < nvfp4::kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
   if (nvfp4::kCoordBytes + 8 * nvfp4::quantize_chunks(rows, cols, p->blocking, p->rounding) >
-      workspace_bytes)
+      nvfp4::kPartialsOffset)   // (never for an accepted shape)
     return NVFP4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
   q.ws = workspace;

@@ -8,10 +8,6 @@
 
 namespace nvfp4 {
 
-// Quantization workspace: a block of coordination words, then one 64-bit word per chunk of
-// the input (see quantize.hip).  8 MiB covers the largest tensor the ABI accepts.
-constexpr size_t kCoordBytes = 8192;
-constexpr size_t kWorkspaceBytes = ((size_t)8 << 20) + kCoordBytes;
 
 // Work division of the quantization kernels (quantize.hip), shared with the argument checks.
 // 1x16, nearest-even: a chunk is kT1 threads x kG1 row groups of 16 elements.
@@ -23,12 +19,23 @@ constexpr uint32_t kAmaxMaxWg = 1024;
 // 16x16: a chunk is up to kG16 tile-rows x 16 tile-columns.
 constexpr int kG16 = 8;
 
-// 64-bit words the quantization workspace needs after its header for a rows x cols tensor
-// (rows, cols >= 0, multiples of 16, rows * cols <= 2^35): one per chunk, or the pass-1
-// partials of stochastic rounding with 1x16 blocks.
+// Quantization workspace (see quantize.hip): a header of coordination words, one 64-bit
+// word per chunk for the single-read kernels (8 MiB covers the largest tensor the ABI
+// accepts: 2^20 chunks of 16x16 blocks), then the pass-1 partial maxima of the two-pass
+// stochastic path in a region of their own, so that no word one path writes is ever read
+// by the other as its own.
+constexpr size_t kCoordBytes = 8192;
+constexpr size_t kWordsBytes = (size_t)8 << 20;
+constexpr size_t kPartialsOffset = kCoordBytes + kWordsBytes;
+constexpr size_t kWorkspaceBytes = kPartialsOffset + 4 * (size_t)kAmaxMaxWg;
+
+// Chunk words the single-read kernels need after the workspace header for a rows x cols
+// tensor (rows, cols >= 0, multiples of 16, rows * cols <= 2^35): one per chunk; none for
+// the two-pass path (stochastic rounding with 1x16 blocks), whose partials have their own
+// region.
 inline uint64_t quantize_chunks(int64_t rows, int64_t cols, int blocking, int rounding) {
   if (blocking == 0) {
-    if (rounding == 1) return (kAmaxMaxWg * 4 + 7) / 8;
+    if (rounding == 1) return 0;
     return ((uint64_t)rows * (uint64_t)(cols / 16) + kChunk1 - 1) / kChunk1;
   }
   return (((uint64_t)(rows / 16) + kG16 - 1) / kG16) * (((uint64_t)(cols / 16) + 15) / 16);

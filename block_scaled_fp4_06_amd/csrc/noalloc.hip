@@ -69,7 +69,7 @@ extern "C" nvfp4_status nvfp4_quantize_noalloc(const uint16_t *x, int64_t rows, 
   if (st != NVFP4_OK) return st;
   // every accepted shape fits the array; the bound is checked all the same
   if (nvfp4::kCoordBytes + 8 * nvfp4::quantize_chunks(rows, cols, p->blocking, p->rounding) >
-      nvfp4::kWorkspaceBytes)
+      nvfp4::kPartialsOffset)
     return NVFP4_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int dev = 0;

@@ -251,56 +251,69 @@ __device__ __forceinline__ const uint4 *group_ptr(const uint16_t *x, uint32_t g,
 }
 
 // Block multipliers for the 127 codes a block scale can take, built once per workgroup:
-// rtab[c] = s_enc / decode(c), 0 for the zero scale.  With quarter set (RHT input), the
-// transform's final 1/4 moves into the table, t * (r / 4) in place of (t / 4) * r, when
-// that is exact for every element; the function returns whether it did.  Both forms round
-// the same real product when t / 4 and r / 4 are exact (r >= 2^-124).  Where t / 4 is not
-// (|t| < 2^-124) and r < 2^108, both products stay below 2^-18 in magnitude with the sign
-// of t: a zero code under nearest rounding, and never a step up under stochastic
-// rounding, whose smallest threshold is 2^-17 of a step.
-__device__ __forceinline__ bool build_rtab(float *rtab, float s_enc, bool quarter) {
+// rtab[c] = s_enc / decode(c), 0 for the zero scale.  Two factors can move into the table
+// when that is exact for every entry; the return value says which did (bit 0, bit 1):
+//  * kFoldQuarter (quarter set, RHT input): the transform's final 1/4, t * (r / 4) in
+//    place of (t / 4) * r.  Both forms round the same real product when t / 4 and r / 4 are
+//    exact (r >= 2^-124).  Where t / 4 is not (|t| < 2^-124) and r < 2^108, both products
+//    stay below 2^-18 in magnitude with the sign of t: a zero code under nearest rounding,
+//    and never a step up under stochastic rounding, whose smallest threshold is 2^-17 of a
+//    step.
+//  * kFold23 (scale23 set, stochastic rounding): the factor 2^23 the stochastic encoder
+//    takes its input in (e2m1_sr_pack16): y * (r 2^23) = (y * r) 2^23 exactly whenever y * r
+//    is a normal binary32; when it is not, both are below 2^-18 (scaled) with the sign of y,
+//    which never rounds up.  Every entry must stay finite: r 2^23 < 2^127.
+constexpr uint32_t kFoldQuarter = 1u, kFold23 = 2u;
+__device__ __forceinline__ uint32_t build_rtab(float *rtab, float s_enc, bool quarter,
+                                               bool scale23) {
   const uint32_t c = threadIdx.x;
   float r = 0.0f;
-  bool ok = true;
+  bool ok = true, ok23 = true;
   if (c < 128u) {
     r = c == 127u ? 0.0f : block_mult(s_enc, e4m3_decode(c));   // 127 is NaN, never made
     ok = r == 0.0f || (r >= 0x1p-124f && r < 0x1p108f);
+    ok23 = r < 0x1p104f;
   }
   const bool all_ok = __syncthreads_and(ok) != 0;
+  const bool all_ok23 = __syncthreads_and(ok23) != 0;
   const bool fold = quarter && all_ok;
-  if (c < 128u) rtab[c] = fold ? 0.25f * r : r;
+  const bool fold23 = scale23 && all_ok23;
+  if (c < 128u) rtab[c] = (fold ? 0.25f * r : r) * (fold23 ? 0x1p23f : 1.0f);
   __syncthreads();
-  return fold;
+  return (fold ? kFoldQuarter : 0u) | (fold23 ? kFold23 : 0u);
 }
 
 // Encode the 16 values of one row group times the block multiplier rr.
-// k[16]: 16-bit random integers (stochastic rounding only).
+// w[8]: the Philox words of the group's draws (stochastic rounding only); scaled23: rr
+// carries the factor 2^23 of the stochastic encoder (kFold23).
 template <bool SR>
-__device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uint32_t k[16]) {
+__device__ __forceinline__ uint2 encode16(const float y[16], float rr, const uint32_t w[8],
+                                          bool scaled23) {
   if (!SR) return e2m1_rn_pack16(y, rr);
-  uint32_t lo = 0, hi = 0;
+  float t[16];
+  if (scaled23) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float a = fabsf(y[j] * rr);
-    const uint32_t mag = e2m1_sr_mag(a, k[j]);
-    const uint32_t q = mag | ((__float_as_uint(y[j]) >> 28) & 8u);
-    if (j < 8) lo |= q << (4 * j);
-    else hi |= q << (4 * (j - 8));
+    for (int j = 0; j < 16; ++j) t[j] = y[j] * rr;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = (y[j] * rr) * 0x1p23f;   // both steps exact
   }
-  return make_uint2(lo, hi);
+  return e2m1_sr_pack16(t, w);
 }
 
-// The 16 random integers of elements idx0 .. idx0+15 (idx0 a multiple of 16): element i
-// takes 16-bit lane (i & 7) of Philox4x32-10(key, counter = (i >> 3, 0, 0)).
+// The Philox words of the draws of elements idx0 .. idx0+15 (idx0 a multiple of 16):
+// element i takes 16-bit lane (i & 7) of Philox4x32-10(key, counter = (i >> 3, 0, 0)), so
+// word j / 2 holds element j's draw (low half for even j, high half for odd j).
 __device__ __forceinline__ void sr_draws(uint64_t idx0, uint32_t k0, uint32_t k1,
-                                         uint32_t k[16]) {
+                                         uint32_t w[8]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint64_t c = (idx0 >> 3) + (uint64_t)h;
     const Philox4 r = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, k0, k1);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) k[8 * h + j] = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    w[4 * h] = r.x;
+    w[4 * h + 1] = r.y;
+    w[4 * h + 2] = r.z;
+    w[4 * h + 3] = r.w;
   }
 }
 
@@ -366,8 +379,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   };
   auto group_max = [&](const uint4 &a, const uint4 &b) __attribute__((always_inline)) {
     float v[16];
-    unpack16(a, b, v);
-    if (RHT) return rht16_absmax_bits(v, sm);
+    unpack16(a, b, v, RHT ? sm : 0u);
+    if (RHT) return rht16_absmax_bits(v);
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   };
   // HAVE_MAX: the chunk phase 1 left in registers, whose group maxima gm[] it kept (the
   // same bits as the maximum of the transformed values here: see rht16_absmax_bits)
-  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold, auto have_max) __attribute__((always_inline)) {
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, uint32_t folds, auto have_max) __attribute__((always_inline)) {
     constexpr bool HAVE_MAX = decltype(have_max)::value != 0;
     const uint32_t base = c * kChunk1;
     static_for<0, kG1>([&](auto I) __attribute__((always_inline)) {
@@ -396,22 +409,22 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       const uint32_t g = base + (uint32_t)i * kT1 + tid;
       if (g < ngroups) {
         float v[16];
-        unpack16(ra[i], rb[i], v);
-        if (RHT) rht16_unscaled(v, sm);           // v = 4 y
+        unpack16(ra[i], rb[i], v, RHT ? sm : 0u);
+        if (RHT) rht16_unscaled(v);           // v = 4 y
         const float amax = HAVE_MAX ? __uint_as_float(gm[i]) : absmax16(v);
         const float bmax = RHT ? amax * 0.25f : amax;
         const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
         const float rr = rtab[sb];
-        if (RHT && !fold) {
+        if (RHT && !(folds & kFoldQuarter)) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
         }
-        uint32_t k[16];
+        uint32_t w[8];
         if (SR) {
           const uint32_t r = g / gpr, gc = g - r * gpr;
-          sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, k);
+          sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, w);
         }
-        put2(codes + (size_t)g * 8u, encode16<SR>(v, rr, k));  // group g at byte 8g
+        put2(codes + (size_t)g * 8u, encode16<SR>(v, rr, w, (folds & kFold23) != 0));  // group g at byte 8g
         put1(scales + g, sb);
       }
     });
@@ -443,12 +456,12 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 
   // phase 2
   if (ts.finite && !failed) {
-    const bool fold = build_rtab(rtab, ts.enc, RHT);
+    const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
-      encode_chunk(last, ts, fold, Idx<1>{});
+      encode_chunk(last, ts, folds, Idx<1>{});
       for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
         load_chunk(c);
-        encode_chunk(c, ts, fold, Idx<0>{});
+        encode_chunk(c, ts, folds, Idx<0>{});
       }
     }
   }
@@ -499,9 +512,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restri
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float v[16];
-      unpack16(a[u], b[u], v);
+      unpack16(a[u], b[u], v, RHT ? sm : 0u);
       if (RHT) {
-        m = max(m, rht16_absmax_bits(v, sm));
+        m = max(m, rht16_absmax_bits(v));
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
@@ -555,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
   }
   const TensorScale ts = finish_amax<RHT>(partials, nparts, global_dec, dev_status, red);
   if (!ts.finite) return;
-  const bool fold = build_rtab(rtab, ts.enc, RHT);
+  const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   for (; g < end; g += kThreads) {
     // next group (on the last step this re-reads the current one: always a valid address)
@@ -563,21 +576,21 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
     const uint4 *pn = group_ptr<CONTIG>(x, gn, gpr, ld);
     const uint4 na = pn[0], nb = pn[1];
     float v[16];
-    unpack16(ca, cb, v);
-    if (RHT) rht16_unscaled(v, sm);           // v = 4 y
+    unpack16(ca, cb, v, RHT ? sm : 0u);
+    if (RHT) rht16_unscaled(v);           // v = 4 y
     const float bmax = RHT ? absmax16(v) * 0.25f : absmax16(v);
     const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
     const float rr = rtab[sb];
-    if (RHT && !fold) {
+    if (RHT && !(folds & kFoldQuarter)) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
     }
-    uint32_t k[16];
+    uint32_t w[8];
     if (SR) {
       const uint32_t r = g / gpr, gc = g - r * gpr;
-      sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, k);
+      sr_draws(sr_base + (uint64_t)r * (uint64_t)cols + (uint64_t)gc * 16u, sk0, sk1, w);
     }
-    put2(codes + (size_t)g * 8u, encode16<SR>(v, rr, k));  // group g at byte 8g
+    put2(codes + (size_t)g * 8u, encode16<SR>(v, rr, w, (folds & kFold23) != 0));  // group g at byte 8g
     put1(scales + g, sb);
     ca = na;
     cb = nb;
@@ -634,7 +647,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
       rb[it] = mask4(p[1], m);
     });
   };
-  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, bool fold) __attribute__((always_inline)) {
+  auto encode_chunk = [&](uint32_t c, const TensorScale &ts, uint32_t folds) __attribute__((always_inline)) {
     const uint32_t br = c / cpr, bc = c - br * cpr;
     const uint32_t tr0 = br * G, nit = min((uint32_t)G, tpc - tr0);
     const uint32_t tc = bc * 16 + tl;
@@ -646,19 +659,19 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         const uint32_t trw = tr0 + it;
         const int64_t row = (int64_t)trw * 16 + r;
         float v[16];
-        unpack16(ra[it], rb[it], v);
-        if (RHT) rht16_unscaled(v, sm);           // v = 4 y
+        unpack16(ra[it], rb[it], v, RHT ? sm : 0u);
+        if (RHT) rht16_unscaled(v);           // v = 4 y
         const uint32_t tmax = row16_max_u32(__float_as_uint(absmax16(v)));
         const float bmax = RHT ? __uint_as_float(tmax) * 0.25f : __uint_as_float(tmax);
         const uint32_t sb = e4m3_encode(div6(bmax) * ts.enc);
         const float rr = rtab[sb];
-        if (RHT && !fold) {
+        if (RHT && !(folds & kFoldQuarter)) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
         }
-        uint32_t k[16];
-        if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, k);
-        uint2 q = encode16<SR>(v, rr, k);
+        uint32_t w[8];
+        if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, w);
+        uint2 q = encode16<SR>(v, rr, w, (folds & kFold23) != 0);
         if (col_ok) {
           *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
           if (r == 0) scales[(size_t)trw * tpr + tc] = (uint8_t)sb;
@@ -694,8 +707,8 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
 
   auto lane_max = [&](const uint4 &a, const uint4 &b) __attribute__((always_inline)) {
     float v[16];
-    unpack16(a, b, v);
-    if (RHT) return rht16_absmax_bits(v, sm);
+    unpack16(a, b, v, RHT ? sm : 0u);
+    if (RHT) return rht16_absmax_bits(v);
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
@@ -740,12 +753,12 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   wg_publish_scale(failed, ts, global_dec, dev_status);
 
   if (ts.finite && !failed) {
-    const bool fold = build_rtab(rtab, ts.enc, RHT);
+    const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
-      encode_chunk(last, ts, fold);
+      encode_chunk(last, ts, folds);
       for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
         load_chunk(c);
-        encode_chunk(c, ts, fold);
+        encode_chunk(c, ts, folds);
       }
     }
   }
@@ -800,8 +813,8 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
 #undef NVFP4_Q1
       return hipGetLastError();
     }
-    // stochastic rounding: two passes, partials after the coordination block
-    uint32_t *partials = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(q.ws) + kCoordBytes);
+    // stochastic rounding: two passes, the partials in their own workspace region
+    uint32_t *partials = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(q.ws) + kPartialsOffset);
     uint32_t nparts = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, kThreads * 4);
     if (nparts > kAmaxMaxWg) nparts = kAmaxMaxWg;
     const uint32_t per_wg = (uint32_t)ceil_div(ngroups64 ? ngroups64 : 1, nparts);
@@ -828,7 +841,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
     const uint64_t tile_rows = (uint64_t)(q.rows / 16), tile_cols = (uint64_t)(q.cols / 16);
     const uint32_t n8 = (uint32_t)quantize_chunks(q.rows, q.cols, 1, q.rounding);
     const uint64_t n4 = ceil_div(tile_rows, 4) * ceil_div(tile_cols, 16);
-    const bool small = kCoordBytes + 8 * n4 <= kWorkspaceBytes;
+    const bool small = kCoordBytes + 8 * n4 <= kPartialsOffset;
 #define NVFP4_Q16G(R, S, T, G, NCH)                                                         \
   do {                                                                                      \
     uint32_t grid = resident_grid<quant_16x16_kernel<R, S, T, G>>(kT16);                    \

@@ -136,7 +136,7 @@ nvfp4_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
  * nvfp4_quantize_noalloc -- nvfp4_quantize without a caller workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The library keeps the workspace in a file-scope device
- * array of nvfp4_quantize_workspace_bytes() bytes (8 MiB + 8 KiB), one per GPU, held until
+ * array of nvfp4_quantize_workspace_bytes() bytes (8 MiB + 12 KiB), one per GPU, held until
  * the process ends; it covers every shape the ABI accepts.  The call allocates nothing.
  *
  * Arguments, results and errors as nvfp4_quantize, without workspace/workspace_bytes.  The

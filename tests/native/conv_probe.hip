@@ -9,7 +9,8 @@
 //   e4m3_decode       fp8 -> fp32;  e4m3_pair_f16: fp8 -> fp16 (the GEMM's block scales);
 //   e2m1_rn_pack16    the scaled fp4 conversion with scale 1.0: nearest-even E2M1 codes;
 //   e2m1_decode_pair  fp4 -> fp32;  dequant8_f16: fp4 -> fp16 times the block scale;
-//   bf16_bits_rn      fp32 -> bf16 nearest-even (the GEMM epilogues).
+//   bf16_bits_rn      fp32 -> bf16 nearest-even (the GEMM epilogues);
+//   e2m1_sr_pack16    the stochastic E2M1 encoder on the hardware stochastic fp4 conversion.
 // Inputs are generated on the device from binary32 bit patterns first + i * stride
 // (modulo 2^32); every entry point launches on the caller's stream and returns the HIP
 // status of the launch.  Grids are grid-stride loops over exactly n items.
@@ -52,6 +53,22 @@ __global__ void bf16_kernel(uint32_t first, uint32_t stride, uint64_t n, uint16_
   for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * kThreads)
     out[i] = nvfp4::bf16_bits_rn(pattern(first, stride, i));
+}
+
+// n16 groups of 16 host-given values v with 16-bit draws k: the stochastic codes of
+// e2m1_sr_pack16, whose input is v * 2^23 and whose draw words hold element 2i's draw in
+// the low and element 2i+1's in the high half of word i.
+__global__ void e2m1_sr_kernel(const float *v, const uint16_t *k, uint64_t n16, uint2 *out) {
+  for (uint64_t g = blockIdx.x * (uint64_t)kThreads + threadIdx.x; g < n16;
+       g += (uint64_t)gridDim.x * kThreads) {
+    float t[16];
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = v[16 * g + j] * 0x1p23f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = k[16 * g + 2 * i] | ((uint32_t)k[16 * g + 2 * i + 1] << 16);
+    out[g] = nvfp4::e2m1_sr_pack16(t, w);
+  }
 }
 
 // Small tables, one thread per entry:
@@ -117,6 +134,11 @@ int probe_e2m1_encode(uint32_t first, uint32_t stride, uint64_t n16, uint8_t *ou
 
 int probe_bf16(uint32_t first, uint32_t stride, uint64_t n, uint16_t *out, hipStream_t s) {
   bf16_kernel<<<grid_for(n), kThreads, 0, s>>>(first, stride, n, out);
+  return (int)hipGetLastError();
+}
+
+int probe_e2m1_sr(const float *v, const uint16_t *k, uint64_t n16, uint8_t *out, hipStream_t s) {
+  e2m1_sr_kernel<<<grid_for(n16), kThreads, 0, s>>>(v, k, n16, reinterpret_cast<uint2 *>(out));
   return (int)hipGetLastError();
 }
 

@@ -3,13 +3,16 @@
 The kernels (1) divide a block amax by 6 with a product and one FMA correction instead
 of a division, (2) take the tensor amax after the RHT without forming the last butterfly
 stage, using max(|a+b|, |a-b|) = |a| + |b| under monotonic rounding, and (3) fold the
-RHT's final 1/4 into the block multiplier; and (4) encode stochastic rounding with one
-formula for every binade of the E2M1 grid.  Each shortcut must give bit-identical
+RHT's final 1/4 into the block multiplier; (4) encode stochastic rounding with the
+hardware stochastic fp4 conversion after rounding |v| up to a multiple of 2^-23; and (5)
+fold that conversion's 2^23 input scale into the block multiplier.  Each shortcut must give bit-identical
 results to the plain form that the oracle evaluates (RHT and scale steps of the NVIDIA
 developer blog "NVFP4 trains with precision of 16-bit ...", section on the pre-training
 quantization recipe).  These are properties of IEEE binary32 arithmetic, checked here on
 the CPU by tests/native/fp_identities.c: exhaustively for (1), on random pairs spanning
-the whole exponent range for (2) and (3).
+the whole exponent range for (2), (3) and (5), and for (4) on a sweep of [0, 6) and every
+decision point (with the conversion modelled as recorded on the GPU; the GPU tests check
+the instruction itself).
 """
 import os
 import subprocess
@@ -50,6 +53,12 @@ def test_quarter_fold(results):
 
 
 def test_stochastic_code_formula(results):
-    # the kernels' single-formula stochastic E2M1 code against the rounding definition
+    # the kernels' stochastic E2M1 encoder (input rounded up to the 2^-23 grid, draw
+    # operand 0xFFFF7C00 - (k << 16), conversion as recorded) against the definition
     n, bad = results["srstep"]
     assert n > 200_000_000 and bad == 0
+
+
+def test_fold23(results):
+    n, bad = results["fold23"]
+    assert n > 5_000_000 and bad == 0

@@ -15,7 +15,12 @@ large input sets; each result is compared with the CPU oracle:
 * bf16_bits_rn (the GEMM epilogues' fp32 -> bf16) on all 2^32 binary32 patterns against
   ``orc_f32_to_bf16`` (itself pinned against torch's cast), NaN compared as NaN;
 * the decoders (fp8 -> fp32 and fp16, fp4 -> fp32, the GEMM's fp4 x scale -> fp16) on
-  every code against ``orc_e4m3_decode`` / ``orc_e2m1_decode`` and their exact product.
+  every code against ``orc_e4m3_decode`` / ``orc_e2m1_decode`` and their exact product;
+* e2m1_sr_pack16, the stochastic encoder on the hardware stochastic fp4 conversion, against
+  ``orc_e2m1_encode_sr`` at every decision point of every 16-bit draw (the exact point,
+  one and two ulps and fractions of a 2^-23 unit on either side, in every grid cell, both
+  signs) and on a sweep of [0, 8) with random draws ([NV-blog] recipe section bullet 5;
+  [PR] outliers section: a value rounds up with probability equal to its position).
 
 The probe is built by ``__graft_entry__.build()``; a GPU run without it fails.
 """
@@ -44,6 +49,8 @@ def probe():
     for name in ("probe_e4m3_encode", "probe_e2m1_encode", "probe_bf16"):
         getattr(L, name).argtypes = [u32, u32, u64, P, P]
         getattr(L, name).restype = ctypes.c_int
+    L.probe_e2m1_sr.argtypes = [P, P, u64, P, P]
+    L.probe_e2m1_sr.restype = ctypes.c_int
     L.probe_tables.argtypes = [P, P, P, P, P, P]
     L.probe_tables.restype = ctypes.c_int
     return L
@@ -172,3 +179,57 @@ def test_decoders_match_oracle(probe):
     nan = np.isnan(ref_dq)
     assert np.array_equal(np.isnan(got_dq), nan)
     assert np.array_equal(got_dq[~nan], ref_dq[~nan])
+
+
+def _sr_decision_cases():
+    """(values, draws): every decision point lo + (2k + 1) step 2^-17 of every draw k in
+    every grid cell, with 1 and 2 ulps and sub-2^-23 offsets on either side (values below 1
+    have finer ulps than the 2^-23 grid the encoder rounds up to), a sweep of [0, 8) with
+    random draws, zeros, saturating values; then all of them negated."""
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4], np.float64)
+    step = np.array([.5, .5, .5, .5, 1, 1, 2], np.float64)
+    k = np.arange(65536, dtype=np.float64)
+    vs, ks = [], []
+    for lo, st in zip(grid, step):
+        t = lo + (2 * k + 1) * st * 2.0 ** -17
+        t32 = t.astype(np.float32)
+        assert np.all(t32.astype(np.float64) == t)   # the decision points are binary32
+        x = t32
+        for d in range(3):
+            up, dn = x.copy(), x.copy()
+            for _ in range(d):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+            vs += [up, dn] if d else [x]
+            ks += [np.arange(65536, dtype=np.uint16)] * (2 if d else 1)
+        for off in (2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26):
+            for sgn in (-1, 1):
+                vs.append((t + sgn * off).astype(np.float32))
+                ks.append(np.arange(65536, dtype=np.uint16))
+    rng = np.random.default_rng(3)
+    sweep = np.arange(0, 0x41000000, 997, dtype=np.uint32).view(np.float32)
+    vs.append(sweep)
+    ks.append(rng.integers(0, 65536, sweep.size).astype(np.uint16))
+    vs.append(np.array([0.0, 6.0, 7.9, 100.0, 1e-30, 2.0 ** -18, 2.0 ** -19, 0.25], np.float32))
+    ks.append(np.array([0, 1, 2, 3, 4, 0, 65535, 32767], np.uint16))
+    v = np.concatenate(vs)
+    kk = np.concatenate(ks)
+    v, kk = np.concatenate([v, -v]), np.concatenate([kk, kk])
+    n = v.size - v.size % 16
+    return np.ascontiguousarray(v[:n]), np.ascontiguousarray(kk[:n])
+
+
+def test_stochastic_encoder_matches_oracle_at_every_decision_point(probe):
+    v, k = _sr_decision_cases()
+    n16 = v.size // 16
+    print("stochastic encoder: %d values" % v.size, flush=True)
+    tv = torch.from_numpy(v).cuda()
+    tk = torch.from_numpy(k.view(np.int16)).cuda()
+    out = torch.empty(n16 * 8, dtype=torch.uint8, device="cuda")
+    assert probe.probe_e2m1_sr(ctypes.c_void_p(tv.data_ptr()), ctypes.c_void_p(tk.data_ptr()),
+                               n16, ctypes.c_void_p(out.data_ptr()), _stream()) == 0
+    got = out.cpu().numpy()
+    ref = _pack(oracle.e2m1_encode_sr(v, k))
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, "%d bytes differ; first: value %r draw %d, gpu %02x oracle %02x" % (
+        bad.size, float(v[2 * bad[0]]), k[2 * bad[0]], got[bad[0]], ref[bad[0]])
