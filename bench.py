@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--summarize", metavar="DIR",
                     help="print the summary of a rocprofv3 output directory (kernel trace "
                          "and/or counters) instead of benchmarking")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/gemm_w5_traffic.json from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of a bench run with --copy-calibration")
     ap.add_argument("--last", type=int, default=0,
                     help="with --summarize: only the last N dispatches of each kernel and "
                          "grid (the timed ones of a run with --steps N)")
@@ -390,8 +393,23 @@ def _field(row, *names):
     return None
 
 
+def _short_name(name):
+    """A kernel's name without the return type, namespaces and argument list."""
+    name = name.replace("void ", "", 1).replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):   # the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return name[:cut].replace("nvfp4::", "")
+
+
 def _kernel_key(row):
-    name = _field(row, "Kernel_Name") or "?"
+    name = _short_name(_field(row, "Kernel_Name") or "?")
     grid = int(_field(row, "Grid_Size_X", "Grid_Size") or 0)
     wg = int(_field(row, "Workgroup_Size_X", "Workgroup_Size") or 0)
     return name, grid, wg
@@ -415,7 +433,7 @@ def summarize(d, last=0):
             groups.setdefault(_kernel_key(r), []).append((t0, (t1 - t0) / 1000.0))
         out.append("rocprofv3 kernel trace: durations in us%s" %
                    (", last %d dispatches of each kernel and grid" % last if last else ""))
-        out.append("%-46s %9s %5s %6s %10s %10s %10s %10s %10s %10s" % (
+        out.append("%-56s %9s %5s %6s %10s %10s %10s %10s %10s %10s" % (
             "kernel", "grid_thr", "wg", "calls", "mean", "median", "p10", "p90", "min", "max"))
         rows = []
         for (name, grid, wg), v in groups.items():
@@ -424,8 +442,8 @@ def summarize(d, last=0):
             rows.append((us.sum(), name, grid, wg, us))
         for _, name, grid, wg, us in sorted(rows, key=lambda t: -t[0]):
             p10, med, p90 = np.percentile(us, [10, 50, 90])
-            out.append("%-46s %9d %5d %6d %10.2f %10.2f %10.2f %10.2f %10.2f %10.2f" % (
-                name[:46], grid, wg, us.size, us.mean(), med, p10, p90, us.min(), us.max()))
+            out.append("%-56s %9d %5d %6d %10.2f %10.2f %10.2f %10.2f %10.2f %10.2f" % (
+                name[:56], grid, wg, us.size, us.mean(), med, p10, p90, us.min(), us.max()))
     ctr = _csv_rows(d, "counter_collection.csv")
     if ctr:
         per = {}   # (kernel key) -> dispatch -> counter -> summed value
@@ -449,26 +467,80 @@ def summarize(d, last=0):
         for c, f in scale.items():
             out.append("calibration: %s counts %.4f of the bytes the 256 MiB copy moves "
                        "(scale x%.4f)" % (c, 1.0 / f, f))
-        hdr = "%-46s %9s %5s" % ("kernel", "grid_thr", "n")
+        mfma = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names
+        if mfma:
+            out.append("MFMA_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 "
+                       "XCDs); GRBM_GUI_ACTIVE also counts the window around a dispatch, so the "
+                       "ratio means something for long dispatches only")
+        hdr = "%-56s %9s %5s" % ("kernel", "grid_thr", "n")
         for c in names:
             hdr += " %16s" % c
             if c in scale:
                 hdr += " %10s" % (c.split("_")[0].lower() + "_MB")
+        if mfma:
+            hdr += " %10s" % "MFMA_busy"
         out.append(hdr)
         for key in sorted(per, key=lambda k: k[0]):
             ds = [per[key][dd] for dd in sorted(per[key])]
             if last:
                 ds = ds[-last:]
-            line = "%-46s %9d %5d" % (key[0][:46], key[1], len(ds))
+            line = "%-56s %9d %5d" % (key[0][:56], key[1], len(ds))
+            meds = {}
             for c in names:
-                med = float(np.median([dd.get(c, 0.0) for dd in ds]))
+                med = meds[c] = float(np.median([dd.get(c, 0.0) for dd in ds]))
                 line += " %16.6g" % med
                 if c in scale:
                     line += " %10.2f" % (med * 1024.0 * scale[c] / 1e6)
+            if mfma:
+                cyc = 1024.0 * meds["GRBM_GUI_ACTIVE"] / 8.0
+                line += " %9.1f%%" % (100.0 * meds["SQ_VALU_MFMA_BUSY_CYCLES"] / cyc if cyc else 0.0)
             out.append(line)
     if not out:
         out.append("no kernel_trace.csv or counter_collection.csv under %s" % d)
     return "\n".join(out)
+
+
+def record_traffic(fetch_dir, write_dir, last=0):
+    """HBM bytes of one workload-5 GEMM launch (the largest grid of gemm256_kernel<false>)
+    from the FETCH_SIZE and WRITE_SIZE counter runs, each scaled by what it reads for the
+    256 MiB calibration copy; written with the GEMM source's hash so that bench.py reports
+    it only while the kernel is unchanged."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    res = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if _field(r, "Counter_Name") != cname:
+                continue
+            key, disp = _kernel_key(r), int(_field(r, "Dispatch_Id", "Correlation_Id") or 0)
+            per.setdefault(key, {}).setdefault(disp, 0.0)
+            per[key][disp] += float(_field(r, "Counter_Value"))
+        copy = max(v for (n, _, _), dd in per.items() if "copyBuffer" in n for v in dd.values())
+        scale = (256 << 20) / 1024.0 / copy
+        gkeys = [k for k in per if k[0].startswith("gemm256_kernel<false>")]
+        gk = max(gkeys, key=lambda k: k[1])
+        vals = [per[gk][dd] for dd in sorted(per[gk])]
+        if last:
+            vals = vals[-last:]
+        res[cname] = (float(np.median(vals)) * 1024.0 * scale, scale, gk[0], len(vals))
+    src = os.path.join(here, "block_scaled_fp4_06_amd", "csrc", "gemm.hip")
+    rec = {"kernel": res["FETCH_SIZE"][2], "workload": "8192x20480x5120 bf16 out",
+           "dispatches": res["FETCH_SIZE"][3],
+           "read_bytes": res["FETCH_SIZE"][0], "write_bytes": res["WRITE_SIZE"][0],
+           "fetch_scale": round(res["FETCH_SIZE"][1], 4), "write_scale": round(res["WRITE_SIZE"][1], 4),
+           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o bench -- python3 "
+                        "bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"
+                        % fetch_dir,
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o bench -- python3 "
+                        "bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"
+                        % write_dir],
+           "traffic_bytes": res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0]}
+    path = os.path.join(here, "profiles", "gemm_w5_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return path
 
 
 def graph_of(fn, calls):
@@ -501,6 +573,9 @@ def main():
     args = parse()
     if args.summarize:
         print(summarize(args.summarize, args.last))
+        return
+    if args.record_traffic:
+        print(record_traffic(*args.record_traffic, last=args.last))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -539,35 +614,55 @@ def main():
         for fn in calls.values():
             fn()
 
+    names = list(calls)
+    flops = 2.0 * M * NN * K
+    work = {"quantize_x": (quant_bytes(M, K, "1x16"), "GB/s"),
+            "quantize_w": (quant_bytes(K, NN, "16x16", True), "GB/s"),
+            "gemm": (flops, "TFLOP/s"),
+            "dequantize_x": (dequant_bytes(M, K, "1x16"), "GB/s")}
+
+    def figures(t_ms, name):
+        by, unit = work[name]
+        if unit == "GB/s":
+            ach = by / (t_ms * 1e-3) / 1e9
+            return {"ms": round(t_ms, 4), "GBps": round(ach, 1),
+                    "frac_hbm": round(ach / HBM_PEAK_GBPS, 4), "bytes": by}
+        ach = by / (t_ms * 1e-3) / 1e12
+        return {"ms": round(t_ms, 4), "TFLOPs": round(ach, 1),
+                "frac_mfma_f16": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                "frac_mfma_fp4_context": round(ach / MFMA_FP4_PEAK_TFLOPS, 4)}
+
+    # each kernel alone: a graph of `steps` back-to-back launches on the same (cache-warm)
+    # input, replayed once untimed and once timed
+    alone = {}
+    for name in names:
+        alone[name] = figures(replay_ms(graph_of(calls[name], args.steps)) / args.steps, name)
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the timed steps replay a captured graph of one step: the four launches run back to
-    # back, so ms_per_step is GPU time, not the host's per-call cost
-    g_step = graph_of(step, 1)
-    log("timing %d steps (graph replays)" % args.steps)
-    ms = replay_ms(g_step, args.steps) / args.steps
-    # per-kernel times: a graph of `steps` back-to-back launches of one kernel, replayed
-    # once untimed and once timed (the last `steps` dispatches of each kernel in a trace of
-    # this run are the timed ones)
-    kern = {}
-    flops = 2.0 * M * NN * K
-    for name, by, unit in (("quantize_x", quant_bytes(M, K, "1x16"), "GB/s"),
-                           ("quantize_w", quant_bytes(K, NN, "16x16", True), "GB/s"),
-                           ("gemm", flops, "TFLOP/s"),
-                           ("dequantize_x", dequant_bytes(M, K, "1x16"), "GB/s")):
-        t = replay_ms(graph_of(calls[name], args.steps)) / args.steps
-        if unit == "GB/s":
-            ach = by / (t * 1e-3) / 1e9
-            kern[name] = {"ms": round(t, 4), "GBps": round(ach, 1),
-                          "frac_hbm": round(ach / HBM_PEAK_GBPS, 4), "bytes": by}
-        else:
-            ach = by / (t * 1e-3) / 1e12
-            kern[name] = {"ms": round(t, 4), "TFLOPs": round(ach, 1),
-                          "frac_mfma_f16": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                          "frac_mfma_fp4_context": round(ach / MFMA_FP4_PEAK_TFLOPS, 4)}
-        log("%s: %.4f ms" % (name, t))
+    # the timed region: a graph of one step, replayed `steps` times back to back (timed
+    # with events around the replays) gives ms_per_step; each kernel's in-step time comes
+    # from events recorded between eager launches of `steps` more steps (the host enqueues
+    # far ahead of a GPU whose steps take milliseconds, and ROCm does not allow timing
+    # events inside a captured graph)
+    log("timing %d steps (graph replay)" % args.steps)
+    how = "events between eager launches of the step"
+    g1 = graph_of(step, 1)
+    ms = replay_ms(g1, args.steps) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        for j, name in enumerate(names):
+            calls[name]()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    kern = {name: figures(sum(evs[i][j].elapsed_time(evs[i][j + 1])
+                              for i in range(args.steps)) / args.steps, name)
+            for j, name in enumerate(names)}
+    for name in names:
+        log("%s: %.4f ms in the step (%.4f ms alone)" % (name, kern[name]["ms"], alone[name]["ms"]))
     g = kern["gemm"]
     out = {
         "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
@@ -583,6 +678,8 @@ def main():
                      "unit": "TFLOP/s", "frac": g["frac_mfma_f16"],
                      "traffic": gemm_traffic_bytes(), "kernel": "gemm"},
         "kernels": kern,
+        "kernel_timing": how,
+        "kernels_alone": alone,
     }
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
