@@ -233,7 +233,10 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
   // slot chunk ^ ((row >> 1) & 7) = chunk ^ (4 (i & 1) + lane/16).  (The direct
   // global->LDS load instructions were measured to cost ~250 cycles of issue each here.)
   // The resources start at the tile's first row and end at the operand's last, so offsets
-  // stay below 256 rows (32-bit for K < 2^24) however large the operands are.
+  // stay below 256 rows (32-bit for K < 2^24) however large the operands are.  The whole
+  // offset of every load is the per-lane offset (the scalar offset is zero): the range
+  // check, which covers the per-lane offset, then sees a row's full address, and a row past
+  // the operand's end is never read.
   const int rows_a = min(p.M - m0, kT2), rows_b = min(p.N - n0, kT2);
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.ac + (int64_t)m0 * rowb, (int64_t)rows_a * rowb);
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.bc + (int64_t)n0 * rowb, (int64_t)rows_b * rowb);
@@ -253,15 +256,14 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
   auto gload_part = [&](int kb, int q) {
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + (kbeg + kb) * kRowB2));
-      sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_code, soff, 0);
-      stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff_code, soff, 0);
+      const int off = voff_code + (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + (kbeg + kb) * kRowB2));
+      sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      stb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
     }
     if (q == 3) {
-      ssa = __builtin_amdgcn_raw_buffer_load_b128(
-          rsa, voff_sa, (int)__builtin_amdgcn_readfirstlane((uint32_t)((kbeg + kb) * 16)), 0);
-      ssb = __builtin_amdgcn_raw_buffer_load_b128(
-          rsb, voff_sb, (int)__builtin_amdgcn_readfirstlane((uint32_t)((kbeg + kb) * 16)), 0);
+      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)((kbeg + kb) * 16));
+      ssa = __builtin_amdgcn_raw_buffer_load_b128(rsa, voff_sa + soff, 0, 0);
+      ssb = __builtin_amdgcn_raw_buffer_load_b128(rsb, voff_sb + soff, 0, 0);
     }
   };
   auto gload = [&](int kb) {

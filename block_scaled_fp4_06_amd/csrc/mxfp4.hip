@@ -248,9 +248,10 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
     const int valid = KFULL ? 8 : min(8, sgr - 8 * kb);
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + kb * kMRowB));
-      g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ga, voff_code, soff, 0);
-      g.b[i] = __builtin_amdgcn_raw_buffer_load_b128(gb, voff_code, soff, 0);
+      // the whole offset in the per-lane offset, which the range check covers
+      const int off = voff_code + (int)__builtin_amdgcn_readfirstlane((uint32_t)(8 * i * rowb + kb * kMRowB));
+      g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ga, off, 0, 0);
+      g.b[i] = __builtin_amdgcn_raw_buffer_load_b128(gb, off, 0, 0);
       if (!KFULL && (lane & 7) >= valid) {
         g.a[i] = (v4i32){0, 0, 0, 0};
         g.b[i] = (v4i32){0, 0, 0, 0};
@@ -260,8 +261,8 @@ __device__ __forceinline__ void mx_tile(const MxGemmParams &p, int tile, int til
     const __amdgpu_buffer_rsrc_t gsa = live ? rsa : r0, gsb = live ? rsb : r0;
     if (KFULL) {
       const int soff = (int)__builtin_amdgcn_readfirstlane((uint32_t)(kb * 8));
-      g.sa = __builtin_amdgcn_raw_buffer_load_b64(gsa, voff_s, soff, 0);
-      g.sb = __builtin_amdgcn_raw_buffer_load_b64(gsb, voff_s, soff, 0);
+      g.sa = __builtin_amdgcn_raw_buffer_load_b64(gsa, voff_s + soff, 0, 0);
+      g.sb = __builtin_amdgcn_raw_buffer_load_b64(gsb, voff_s + soff, 0, 0);
     } else {
       // the scale rows of a K that is not a multiple of 256 are not 8-byte aligned
       uint32_t a2[2] = {0u, 0u}, b2[2] = {0u, 0u};
