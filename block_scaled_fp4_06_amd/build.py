@@ -37,16 +37,27 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(out: str = LIB, extra=()) -> str:
-    """Compile every source to an object (in parallel, one hipcc per file), then link."""
+def build(out: str = LIB, extra=(), timeline_out: str | None = None) -> str:
+    """Compile every source to an object (in parallel, one hipcc per file), then link.
+
+    timeline_out: also link a test-only variant of the library there, whose quantize
+    kernels are compiled with NVFP4_TIMELINE (phase timestamps; nvfp4_timeline_attach)."""
     tmp = out + ".tmp%d" % os.getpid()
     objs, procs = [], []
+
+    def compile_(src, obj, more=()):
+        cmd = [hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra) + list(more) + [
+            "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", obj, src]
+        procs.append((src, subprocess.Popen(cmd, cwd=ROOT)))
+
     for src in sources():
         obj = "%s.%d.o" % (out, len(objs))
         objs.append(obj)
-        cmd = [hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra) + [
-            "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", obj, src]
-        procs.append((src, subprocess.Popen(cmd, cwd=ROOT)))
+        compile_(src, obj)
+    tl_obj = None
+    if timeline_out:
+        tl_obj = "%s.timeline.o" % out
+        compile_(os.path.join(CSRC, "quantize.hip"), tl_obj, ["-DNVFP4_TIMELINE=1"])
     try:
         for src, pr in procs:
             if pr.wait() != 0:
@@ -54,11 +65,18 @@ def build(out: str = LIB, extra=()) -> str:
         subprocess.check_call([hipcc()] + HIPCC_FLAGS + list(extra) + ["-o", tmp] + objs,
                               cwd=ROOT)
         os.replace(tmp, out)
+        if timeline_out:
+            qobj = objs[sources().index(os.path.join(CSRC, "quantize.hip"))]
+            tl_objs = [tl_obj if o == qobj else o for o in objs]
+            tmp2 = timeline_out + ".tmp%d" % os.getpid()
+            subprocess.check_call([hipcc()] + HIPCC_FLAGS + list(extra) + ["-o", tmp2] + tl_objs,
+                                  cwd=ROOT)
+            os.replace(tmp2, timeline_out)
     finally:
         for pr in procs:
             if pr[1].poll() is None:
                 pr[1].kill()
-        for o in objs:
+        for o in objs + ([tl_obj] if tl_obj else []):
             if os.path.exists(o):
                 os.remove(o)
     return out

@@ -32,6 +32,31 @@
 namespace nvfp4 {
 namespace {
 
+// ---------------------------------------------------------------- phase timeline
+// Built with NVFP4_TIMELINE (a test-only variant of the library, never the product): each
+// workgroup's first thread records the constant 100 MHz clock at the phase boundaries
+// into the buffer nvfp4_timeline_attach() names, region `kind` (one per kernel), four
+// stamps per workgroup: start, own chunks' maxima published (or partials written), tensor
+// amax known, end (after a workgroup barrier).  Stamps a kernel has no such boundary for
+// stay as the caller left them.
+constexpr uint32_t kTlWgs = 8192;   // workgroups per region
+#ifdef NVFP4_TIMELINE
+__device__ uint64_t *g_timeline = nullptr;
+__device__ __forceinline__ void tl_stamp(uint32_t kind, uint32_t i) {
+  uint64_t *t = g_timeline;
+  if (t && threadIdx.x == 0 && blockIdx.x < kTlWgs)
+    t[((size_t)kind * kTlWgs + blockIdx.x) * 4 + i] = (uint64_t)wall_clock64();
+}
+__device__ __forceinline__ void tl_end(uint32_t kind) {
+  __syncthreads();
+  tl_stamp(kind, 3);
+}
+#else
+__device__ __forceinline__ void tl_stamp(uint32_t, uint32_t) {}
+__device__ __forceinline__ void tl_end(uint32_t) {}
+#endif
+enum : uint32_t { kTlFused1x16 = 0, kTl16x16 = 1, kTlAmax = 2, kTlSr = 3 };
+
 // ---------------------------------------------------------------- coordination
 // Workspace: the header, then one uint64_t word per chunk at kCoordBytes.  The tag of a
 // launch is epoch + 1, read by every workgroup when it starts.  After its phase 1 each
@@ -359,6 +384,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   uint64_t *gword = &hdr->gword;
   uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
   const uint32_t tok = wg_tag(hdr, slot);
+  tl_stamp(kTlFused1x16, 0);
   const uint32_t tid = threadIdx.x;
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   constexpr bool SR = false;   // stochastic rounding takes the two-pass kernels below
@@ -444,6 +470,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (tid == 0) store_relaxed(words + c, tagged(tok, m));
     last = c;
   }
+  tl_stamp(kTlFused1x16, 1);
 
   wg_arrive<kT1>(hdr, tok);
 
@@ -453,6 +480,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
   const TensorScale ts = tensor_scale(am);
   wg_publish_scale(failed, ts, global_dec, dev_status);
+  tl_stamp(kTlFused1x16, 2);
 
   // phase 2
   if (ts.finite && !failed) {
@@ -465,6 +493,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
     }
   }
+  tl_end(kTlFused1x16);
 }
 
 // ---------------------------------------------------------------- 1x16, stochastic
@@ -490,6 +519,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restri
                                                         uint32_t rk1, uint32_t per_wg,
                                                         uint32_t *__restrict__ partials) {
   __shared__ uint32_t red[kThreads / 64];
+  tl_stamp(kTlAmax, 0);
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
@@ -523,6 +553,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restri
   }
   m = wg_max<kThreads>(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  tl_stamp(kTlAmax, 1);
+  tl_end(kTlAmax);
 }
 
 // Reduce the partial maxima of pass 1 and publish the tensor scale (workgroup 0).
@@ -555,6 +587,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
   constexpr bool SR = true;
   __shared__ float rtab[128];
   __shared__ uint32_t red[kThreads / 64];
+  tl_stamp(kTlSr, 0);
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
   uint32_t g = begin + threadIdx.x;
@@ -567,6 +600,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
     cb = p[1];
   }
   const TensorScale ts = finish_amax<RHT>(partials, nparts, global_dec, dev_status, red);
+  tl_stamp(kTlSr, 2);
   if (!ts.finite) return;
   const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
   const uint32_t sm = RHT ? rht_signmask(rk0, rk1) : 0u;
@@ -595,6 +629,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
     ca = na;
     cb = nb;
   }
+  tl_end(kTlSr);
 }
 
 // ---------------------------------------------------------------- 16x16
@@ -623,6 +658,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   uint64_t *gword = &hdr->gword;
   uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
   const uint32_t tok = wg_tag(hdr, slot);
+  tl_stamp(kTl16x16, 0);
   const uint32_t tpr = (uint32_t)(cols >> 4);          // tiles per tile-row
   const uint32_t tpc = (uint32_t)(rows >> 4);          // tiles per tile-column
   const uint32_t cpr = (tpr + 15) >> 4;                // chunks per chunk-row
@@ -743,6 +779,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     if (threadIdx.x == 0) store_relaxed(words + c, tagged(tok, m));
     last = c;
   }
+  tl_stamp(kTl16x16, 1);
 
   wg_arrive<kT16>(hdr, tok);
 
@@ -751,6 +788,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
   const TensorScale ts = tensor_scale(am);
   wg_publish_scale(failed, ts, global_dec, dev_status);
+  tl_stamp(kTl16x16, 2);
 
   if (ts.finite && !failed) {
     const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
@@ -762,6 +800,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
       }
     }
   }
+  tl_end(kTl16x16);
 }
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
@@ -786,6 +825,14 @@ uint32_t resident_grid(int threads) {
 }
 
 }  // namespace
+
+#ifdef NVFP4_TIMELINE
+// Test-only (timeline builds): the stamp buffer, 4 * kTlWgs uint64 per region, regions
+// 0..3 = fused 1x16, 16x16, amax pass, stochastic pass 2; NULL detaches.
+extern "C" int nvfp4_timeline_attach(uint64_t *buf) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &buf, sizeof(buf));
+}
+#endif
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream) {
   const bool rht = q.rht != 0, sr = q.rounding == 1;
