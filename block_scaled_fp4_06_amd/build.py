@@ -51,12 +51,12 @@ def build(out: str = LIB, extra=(), timeline_out: str | None = None) -> str:
         procs.append((src, subprocess.Popen(cmd, cwd=ROOT)))
 
     for src in sources():
-        obj = "%s.%d.o" % (out, len(objs))
+        obj = "%s.%d.%d.o" % (out, os.getpid(), len(objs))
         objs.append(obj)
         compile_(src, obj)
     tl_obj = None
     if timeline_out:
-        tl_obj = "%s.timeline.o" % out
+        tl_obj = "%s.%d.timeline.o" % (out, os.getpid())
         compile_(os.path.join(CSRC, "quantize.hip"), tl_obj, ["-DNVFP4_TIMELINE=1"])
     try:
         for src, pr in procs:

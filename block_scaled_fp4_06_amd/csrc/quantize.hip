@@ -14,8 +14,9 @@
 //            registers and publishes the chunk's partial amax (integer max of |y| bit
 //            patterns: exact and order-free) as one 64-bit word, (launch tag << 32) | amax,
 //            in the caller's workspace;
-//   collect  workgroup 0 reads every chunk's word and publishes the tensor amax the same
-//            way; the others poll that one word;
+//   collect  every workgroup reads all chunk words when the grid is small; otherwise
+//            workgroup 0 reads them and publishes the tensor amax the same way, in a few
+//            copies of one word that the others poll;
 //   phase 2  every workgroup encodes the chunk still held in its registers, then re-reads
 //            and encodes any other chunk it owns.
 // Words written by an earlier launch carry another tag, so the words are never cleared;
@@ -39,8 +40,8 @@ namespace {
 // stamps per workgroup: start, own chunks' maxima published (or partials written), tensor
 // amax known, end (after a workgroup barrier).  Stamps a kernel has no such boundary for
 // stay as the caller left them.
-constexpr uint32_t kTlWgs = 8192;   // workgroups per region
 #ifdef NVFP4_TIMELINE
+constexpr uint32_t kTlWgs = 8192;   // workgroups per region
 __device__ uint64_t *g_timeline = nullptr;
 __device__ __forceinline__ void tl_stamp(uint32_t kind, uint32_t i) {
   uint64_t *t = g_timeline;
@@ -66,13 +67,17 @@ enum : uint32_t { kTlFused1x16 = 0, kTl16x16 = 1, kTlAmax = 2, kTlSr = 3 };
 // epoch by then.  So every launch, a replay of a captured graph included, gets a tag that
 // no word of the previous launch has.  The workspace must be zero-filled before its first
 // use; the counters return to zero at the end of every launch.
+// The tensor amax that workgroup 0 collects is published in kGCopies words, each on its
+// own 128-byte line, and workgroup b polls copy b % kGCopies: a thousand workgroups polling
+// one word queue on the one cache channel that holds it.
 constexpr uint32_t kArriveGroups = 32;
+constexpr uint32_t kGCopies = 16;
 struct Header {
-  uint64_t gword;    // tensor amax of the current launch, tagged
   uint32_t epoch;    // tag of the last launch whose workgroups all arrived
   uint32_t top;      // groups of the current launch whose workgroups all arrived
-  uint32_t pad[28];
+  uint32_t pad[30];
   struct alignas(128) Line { uint32_t n; } sub[kArriveGroups];   // arrivals per group
+  struct alignas(128) GLine { uint64_t w; } gword[kGCopies];      // tensor amax, tagged
 };
 static_assert(sizeof(Header) <= kCoordBytes, "workspace header");
 template <typename U>
@@ -161,8 +166,11 @@ __device__ __forceinline__ void wg_arrive(Header *h, uint32_t tok) {
 
 // Collect the tensor amax from the chunk words.  partial(c) computes chunk c's partial
 // maximum with the whole workgroup (used only for chunks still missing after the help
-// delay).  Each thread follows its own words c = tid + k*T; the returned value is the
-// same in every thread.
+// delay).  Each thread follows its own words c = tid + k*T in order: it reads up to 8
+// ahead, and a word not yet ready it polls alone, one load in flight, with no
+// workgroup-wide step between polls; the workgroup synchronises when every thread has all
+// its words or has waited past the help delay.  The returned value is the same in every
+// thread.
 template <int T, typename Partial>
 __device__ __forceinline__ uint32_t wg_collect(uint64_t *words, uint32_t nchunks, uint32_t tok,
                                                uint64_t help, uint32_t *red, uint32_t *slot,
@@ -172,8 +180,8 @@ __device__ __forceinline__ uint32_t wg_collect(uint64_t *words, uint32_t nchunks
   const uint64_t t0 = (uint64_t)wall_clock64();   // thread 0's reading decides for all
   *failed = false;
   for (;;) {
-    // read ahead: up to 8 words in flight per thread
     while (next < nchunks) {
+      // read ahead: up to 8 words in flight per thread
       uint64_t w[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -189,7 +197,20 @@ __device__ __forceinline__ uint32_t wg_collect(uint64_t *words, uint32_t nchunks
         }
       }
       next += (uint32_t)ready * T;
-      if (ready < 8) break;
+      if (ready == 8 || next >= nchunks) continue;
+      // word `next` is not ready: poll it alone until it is, or the help delay passes
+      bool got = false;
+      while ((uint64_t)wall_clock64() - t0 < help) {
+        __builtin_amdgcn_s_sleep(1);
+        const uint64_t v = load_relaxed(words + next);
+        if (has_tag(v, tok)) {
+          m = max(m, (uint32_t)v);
+          got = true;
+          break;
+        }
+      }
+      if (!got) break;
+      next += T;
     }
     const uint32_t pending = wg_min<T>(next < nchunks ? next : kNone, red);
     if (pending == kNone) break;
@@ -218,25 +239,26 @@ __device__ __forceinline__ uint32_t wg_collect(uint64_t *words, uint32_t nchunks
 
 // The tensor amax.  When every workgroup can afford to read all chunk words (at most
 // 64K words over the grid per polling round) each collects it directly; otherwise
-// workgroup 0 collects and publishes it in the global word, which the others poll, and
-// a workgroup that has waited past the help delay collects it itself.
+// workgroup 0 collects and publishes it in the kGCopies copies of the global word, which
+// the others poll, and a workgroup that has waited past the help delay collects it itself.
 template <int T, typename Partial>
-__device__ __forceinline__ uint32_t wg_amax(uint64_t *gword, uint64_t *words, uint32_t nchunks,
+__device__ __forceinline__ uint32_t wg_amax(Header *hdr, uint64_t *words, uint32_t nchunks,
                                             uint32_t tok, uint64_t help, uint32_t *red,
                                             uint32_t *slot, bool *failed, Partial &&partial) {
   if ((uint64_t)gridDim.x * nchunks <= 65536u)
     return wg_collect<T>(words, nchunks, tok, help, red, slot, failed, partial);
   if (blockIdx.x == 0) {
     const uint32_t m = wg_collect<T>(words, nchunks, tok, help, red, slot, failed, partial);
-    if (threadIdx.x == 0 && !*failed) store_relaxed(gword, tagged(tok, m));
+    if (threadIdx.x < kGCopies && !*failed) store_relaxed(&hdr->gword[threadIdx.x].w, tagged(tok, m));
     return m;
   }
   if (threadIdx.x == 0) {
+    const uint64_t *gw = &hdr->gword[blockIdx.x % kGCopies].w;
     const uint64_t t0 = (uint64_t)wall_clock64();
-    uint64_t g = load_relaxed(gword);
+    uint64_t g = load_relaxed(gw);
     while (!has_tag(g, tok) && (uint64_t)wall_clock64() - t0 < help) {
-      __builtin_amdgcn_s_sleep(2);
-      g = load_relaxed(gword);
+      __builtin_amdgcn_s_sleep(1);
+      g = load_relaxed(gw);
     }
     slot[0] = has_tag(g, tok) ? 1u : 0u;
     slot[1] = (uint32_t)g;
@@ -381,7 +403,6 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __shared__ uint32_t red[kT1 / 64];
   __shared__ uint32_t slot[2];
   Header *hdr = static_cast<Header *>(ws);
-  uint64_t *gword = &hdr->gword;
   uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
   const uint32_t tok = wg_tag(hdr, slot);
   tl_stamp(kTlFused1x16, 0);
@@ -476,7 +497,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 
   // tensor scale
   bool failed;
-  uint32_t am = wg_amax<kT1>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  uint32_t am = wg_amax<kT1>(hdr, words, nchunks, tok, help, red, slot, &failed, partial);
   if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
   const TensorScale ts = tensor_scale(am);
   wg_publish_scale(failed, ts, global_dec, dev_status);
@@ -557,13 +578,29 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restri
   tl_end(kTlAmax);
 }
 
+// Pass 1's partial maxima, at most kAmaxMaxWg: this thread's share, loaded before anything
+// else the workgroup loads (loads return in order, so the reduction does not wait behind
+// the input stream).
+constexpr int kPartsPerThread = (kAmaxMaxWg + kThreads - 1) / kThreads;
+struct PartialShare { uint32_t v[kPartsPerThread]; };
+__device__ __forceinline__ PartialShare load_partials(const uint32_t *__restrict__ partials,
+                                                      uint32_t nparts) {
+  PartialShare p;
+#pragma unroll
+  for (int k = 0; k < kPartsPerThread; ++k) {
+    const uint32_t i = threadIdx.x + (uint32_t)k * kThreads;
+    p.v[k] = i < nparts ? partials[i] : 0u;
+  }
+  return p;
+}
+
 // Reduce the partial maxima of pass 1 and publish the tensor scale (workgroup 0).
 template <bool RHT>
-__device__ __forceinline__ TensorScale finish_amax(const uint32_t *__restrict__ partials,
-                                                   uint32_t nparts, float *global_dec,
+__device__ __forceinline__ TensorScale finish_amax(const PartialShare &p, float *global_dec,
                                                    uint32_t *dev_status, uint32_t *red) {
   uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, partials[i]);
+#pragma unroll
+  for (int k = 0; k < kPartsPerThread; ++k) m = max(m, p.v[k]);
   m = wg_max<kThreads>(m, red);
   if (RHT && m < 0x7F800000u) m = __float_as_uint(__uint_as_float(m) * 0.25f);
   const TensorScale ts = tensor_scale(m);
@@ -591,6 +628,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, ngroups);
   uint32_t g = begin + threadIdx.x;
+  const PartialShare parts = load_partials(partials, nparts);
   // the first group's load is in flight while the tensor scale is reduced (an empty
   // tensor has no group to load: its workgroup only publishes the tensor scale)
   uint4 ca = make_uint4(0u, 0u, 0u, 0u), cb = ca;
@@ -599,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
     ca = p[0];
     cb = p[1];
   }
-  const TensorScale ts = finish_amax<RHT>(partials, nparts, global_dec, dev_status, red);
+  const TensorScale ts = finish_amax<RHT>(parts, global_dec, dev_status, red);
   tl_stamp(kTlSr, 2);
   if (!ts.finite) return;
   const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
@@ -655,7 +693,6 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   __shared__ uint32_t red[kT16 / 64];
   __shared__ uint32_t slot[2];
   Header *hdr = static_cast<Header *>(ws);
-  uint64_t *gword = &hdr->gword;
   uint64_t *words = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + kCoordBytes);
   const uint32_t tok = wg_tag(hdr, slot);
   tl_stamp(kTl16x16, 0);
@@ -784,7 +821,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   wg_arrive<kT16>(hdr, tok);
 
   bool failed;
-  uint32_t am = wg_amax<kT16>(gword, words, nchunks, tok, help, red, slot, &failed, partial);
+  uint32_t am = wg_amax<kT16>(hdr, words, nchunks, tok, help, red, slot, &failed, partial);
   if (RHT && am < 0x7F800000u) am = __float_as_uint(__uint_as_float(am) * 0.25f);
   const TensorScale ts = tensor_scale(am);
   wg_publish_scale(failed, ts, global_dec, dev_status);
