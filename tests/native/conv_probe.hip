@@ -10,7 +10,8 @@
 //   e2m1_rn_pack16    the scaled fp4 conversion with scale 1.0: nearest-even E2M1 codes;
 //   e2m1_decode_pair  fp4 -> fp32;  dequant8_f16: fp4 -> fp16 times the block scale;
 //   bf16_bits_rn      fp32 -> bf16 nearest-even (the GEMM epilogues);
-//   e2m1_sr_pack16    the stochastic E2M1 encoder on the hardware stochastic fp4 conversion.
+//   e2m1_sr_pack16    the stochastic E2M1 encoder on the hardware stochastic fp4 conversion;
+//   and the fp4 -> fp16 conversion's own scale operand, which the GEMM leaves at 1.0.
 // Inputs are generated on the device from binary32 bit patterns first + i * stride
 // (modulo 2^32); every entry point launches on the caller's stream and returns the HIP
 // status of the launch.  Grids are grid-stride loops over exactly n items.
@@ -117,6 +118,22 @@ __global__ void tables_kernel(float *e4m3_dec, float *e2m1_dec, uint32_t *scale_
   }
 }
 
+// The fp4 -> fp16 conversion with a scale operand other than 1.0: code c in all eight
+// positions of a dword, converted with scale s[k]; out[16 k + c] holds the four packed
+// result registers (8 fp16).  One thread per (k, c); n = 16 * number of scales.
+__global__ void scale_operand_kernel(const float *s, uint32_t n, uint4 *out) {
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= n) return;
+  const float sc = s[t >> 4];
+  const uint32_t w = (t & 15u) * 0x11111111u;
+  const nvfp4::half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
+  const nvfp4::half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
+  const nvfp4::half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
+  const nvfp4::half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+  out[t] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                      __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,6 +156,13 @@ int probe_bf16(uint32_t first, uint32_t stride, uint64_t n, uint16_t *out, hipSt
 
 int probe_e2m1_sr(const float *v, const uint16_t *k, uint64_t n16, uint8_t *out, hipStream_t s) {
   e2m1_sr_kernel<<<grid_for(n16), kThreads, 0, s>>>(v, k, n16, reinterpret_cast<uint2 *>(out));
+  return (int)hipGetLastError();
+}
+
+int probe_scale_operand(const float *s, uint32_t nscales, uint8_t *out, hipStream_t st) {
+  const uint32_t n = 16u * nscales;
+  scale_operand_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, st>>>(
+      s, n, reinterpret_cast<uint4 *>(out));
   return (int)hipGetLastError();
 }
 

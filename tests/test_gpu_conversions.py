@@ -20,7 +20,10 @@ large input sets; each result is compared with the CPU oracle:
   ``orc_e2m1_encode_sr`` at every decision point of every 16-bit draw (the exact point,
   one and two ulps and fractions of a 2^-23 unit on either side, in every grid cell, both
   signs) and on a sweep of [0, 8) with random draws ([NV-blog] recipe section bullet 5;
-  [PR] outliers section: a value rounds up with probability equal to its position).
+  [PR] outliers section: a value rounds up with probability equal to its position);
+* the fp4 -> fp16 conversion's own scale operand: it applies only the power of two of the
+  scale (1.5 acts as 1, 3 as 2, 448 as 256), which is why the GEMM converts with scale 1.0
+  and multiplies by the E4M3 block scale in a separate packed fp16 product.
 
 The probe is built by ``__graft_entry__.build()``; a GPU run without it fails.
 """
@@ -53,6 +56,8 @@ def probe():
     L.probe_e2m1_sr.restype = ctypes.c_int
     L.probe_tables.argtypes = [P, P, P, P, P, P]
     L.probe_tables.restype = ctypes.c_int
+    L.probe_scale_operand.argtypes = [P, u32, P, P]
+    L.probe_scale_operand.restype = ctypes.c_int
     return L
 
 
@@ -233,3 +238,21 @@ def test_stochastic_encoder_matches_oracle_at_every_decision_point(probe):
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, "%d bytes differ; first: value %r draw %d, gpu %02x oracle %02x" % (
         bad.size, float(v[2 * bad[0]]), k[2 * bad[0]], got[bad[0]], ref[bad[0]])
+
+
+def test_fp4_conversion_scale_operand_applies_only_its_power_of_two(probe):
+    # every code, in all eight positions, converted with scales that carry a mantissa: the
+    # result is the code's value times 2^floor(log2 scale), not times the scale
+    scales = np.array([1.0, 1.25, 1.5, 1.875, 2.0, 3.0, 0.375, 448.0, 0.125, 6.0, 1.5 * 2.0 ** -9],
+                      dtype=np.float32)
+    s = torch.from_numpy(scales).cuda()
+    out = torch.empty(16 * len(scales) * 16, dtype=torch.uint8, device="cuda")
+    assert probe.probe_scale_operand(s.data_ptr(), len(scales), out.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float16).reshape(len(scales), 16, 8).astype(np.float64)
+    codes = np.arange(16)
+    val = oracle.e2m1_decode(codes).astype(np.float64)
+    for k, sc in enumerate(scales):
+        p2 = 2.0 ** np.floor(np.log2(np.float64(sc)))
+        want = np.repeat((val * p2)[:, None], 8, axis=1)
+        assert np.array_equal(got[k], want), (sc, got[k][:, 0], want[:, 0])
