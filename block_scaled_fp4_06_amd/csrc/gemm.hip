@@ -307,10 +307,13 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
   // the loads of step kb+2 go into the freed stage and the first operands of step kb+1
   // are prepared under the last MFMAs of step kb.
   uint4 ca[2][4], cb[2][4];      // packed codes of two 32-element chunks (double buffer)
+  uint32_t sra[2][4], srb[2][4]; // their scale dwords, as read
   half2_t hsa[2][4], hsb[2][4];  // their block scales
   half8_t ao[2][4], bo[2][4];    // dequantized operands of two sub-steps
-  // chunk j of a stage: 16 code bytes per block row and the two scale bytes (K groups
-  // 4j + 2h, 4j + 2h + 1) that cover them, into buffer j & 1
+  // chunk j of a stage: 16 code bytes per block row and the dword of scale bytes that holds
+  // the two (K groups 4j + 2h, 4j + 2h + 1) covering them, into buffer j & 1; the scales
+  // are converted by convert_scales a sub-step later, so that no instruction waits for
+  // these LDS reads right after they are issued
   auto load_chunk16 = [&](const uint8_t *st, int j) {
     const int slot = ((2 * j + h) ^ ((l32 >> 1) & 7)) * 16;
     const uint8_t *ssa = st + 2 * kCodesB2, *ssb = ssa + kScalesB2;
@@ -319,10 +322,15 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
     for (int i = 0; i < 4; ++i) {
       ca[b][i] = lds16(st + (wm * 128 + i * 32 + l32) * kRowB2 + slot);
       cb[b][i] = lds16(st + kCodesB2 + (wn * 128 + i * 32 + l32) * kRowB2 + slot);
-      const uint32_t wa = *reinterpret_cast<const uint32_t *>(ssa + j * 1024 + (wm * 128 + i * 32 + l32) * 4);
-      const uint32_t wb = *reinterpret_cast<const uint32_t *>(ssb + j * 1024 + (wn * 128 + i * 32 + l32) * 4);
-      hsa[b][i] = e4m3_pair_f16(wa, h);
-      hsb[b][i] = e4m3_pair_f16(wb, h);
+      sra[b][i] = *reinterpret_cast<const uint32_t *>(ssa + j * 1024 + (wm * 128 + i * 32 + l32) * 4);
+      srb[b][i] = *reinterpret_cast<const uint32_t *>(ssb + j * 1024 + (wn * 128 + i * 32 + l32) * 4);
+    }
+  };
+  auto convert_scales = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hsa[b][i] = e4m3_pair_f16(sra[b][i], h);
+      hsb[b][i] = e4m3_pair_f16(srb[b][i], h);
     }
   };
   auto dequant_step = [&](int s, half8_t (&ad)[4], half8_t (&bd)[4]) {
@@ -350,6 +358,7 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
   if (nk > 2) gload(2);   // held in registers until stage 0 is free
   __syncthreads();
   load_chunk16(lds, 0);
+  convert_scales(0);
   dequant_step(0, ao[0], bo[0]);
   for (int kb = 0; kb < nk; ++kb) {
     const uint8_t *st = lds + (kb & 1) * kStageB2;
@@ -358,6 +367,8 @@ void gemm256_kernel(GemmParams p, int tiles_m, int tiles_n, int t_dp, int splits
     for (int s = 0; s < 16; ++s) {
       const int cur = s & 1;
       if ((s & 3) == 0 && s < 12) load_chunk16(st, (s >> 2) + 1);
+      // the chunk read one sub-step ago (at s = 12, chunk 0 of the next step): its scales
+      if ((s & 3) == 1) convert_scales(((s >> 2) + 1) & 1);
       if (s == 11) __syncthreads();   // every wave is done with st; step kb+1's writes are visible
       // step kb+2 into the freed stage, one quarter per sub-step from 11 on; each quarter's
       // registers then take the same quarter of step kb+3
