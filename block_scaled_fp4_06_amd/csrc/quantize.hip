@@ -18,7 +18,7 @@
 //            workgroup 0 reads them and publishes the tensor amax the same way, in a few
 //            copies of one word that the others poll;
 //   phase 2  every workgroup encodes the chunk still held in its registers, then re-reads
-//            and encodes any other chunk it owns.
+//            and encodes any other chunk it owns, newest first.
 // Words written by an earlier launch carry another tag, so the words are never cleared;
 // the only shared read-modify-write is one arrival count per workgroup, off the critical
 // path (an atomic or a fence on a shared address costs about 10 ns per workgroup on this
@@ -508,7 +508,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
       encode_chunk(last, ts, folds, Idx<1>{});
-      for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
+      // the other owned chunks, newest first: the most recently read input is the most
+      // likely to still be in the Infinity Cache
+      for (uint32_t c = last; c >= gridDim.x;) {
+        c -= gridDim.x;
         load_chunk(c);
         encode_chunk(c, ts, folds, Idx<0>{});
       }
@@ -831,7 +834,10 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     const uint32_t folds = build_rtab(rtab, ts.enc, RHT, SR);
     if (last != kNone) {   // a workgroup owns no chunk only when the tensor is empty
       encode_chunk(last, ts, folds);
-      for (uint32_t c = blockIdx.x; c < last; c += gridDim.x) {
+      // the other owned chunks, newest first: the most recently read input is the most
+      // likely to still be in the Infinity Cache (workload-5 weight: 118 -> 111 us)
+      for (uint32_t c = last; c >= gridDim.x;) {
+        c -= gridDim.x;
         load_chunk(c);
         encode_chunk(c, ts, folds);
       }
