@@ -1,0 +1,110 @@
+"""Hardware ceilings the kernels are measured against (GPU, test-only microbenchmarks).
+
+tests/native/hw_probe.hip times, on the box, the rates that the roofline figures of the
+library are read against:
+
+* the fp16 matrix-core instruction stream of the NVFP4 GEMM alone (its 256 x 256 tiles,
+  128 x 128 per wave, v_mfma_f32_32x32x16_f16 on register-resident operands), over the
+  FLOPs of the 8192 x 20480 x 5120 product, with random values shaped like dequantized
+  NVFP4 elements, with zeros, and with the values of the workload-5 operands themselves:
+  what the chip sustains under its power limit, against the 2.5 PFLOP/s dense fp16 figure;
+* streaming HBM reads of the 84 MB activation tensor and streaming writes of 16-64 MiB with
+  ordinary, non-temporal and write-through stores;
+* the cost of one back-to-back launch of an empty kernel.
+
+Each case prints its figure; the assertions only bound them loosely (a broken probe, not a
+slow box, fails).  The probe is built by ``__graft_entry__.build()``.
+"""
+import ctypes
+import os
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROBE = os.path.join(ROOT, "tests", "native", "libhw_probe.so")
+GEMM_FLOP = 2.0 * 8192 * 20480 * 5120
+FP16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBPS = 8000.0
+
+
+@pytest.fixture(scope="module")
+def hwp():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.init()
+    if not os.path.exists(PROBE):
+        pytest.fail("tests/native/libhw_probe.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(PROBE)
+    i32, u64, d = ctypes.c_int, ctypes.c_uint64, ctypes.c_double
+    L.hwp_mfma_stream.argtypes = [i32, i32, i32, i32]
+    L.hwp_read.argtypes = [u64, i32, i32, i32]
+    L.hwp_write.argtypes = [u64, i32, i32, i32]
+    L.hwp_empty.argtypes = [i32, i32]
+    P = ctypes.c_void_p
+    L.hwp_mfma_stream_operands.argtypes = [P, P, P, P, i32, i32, i32, i32, i32]
+    for f in (L.hwp_mfma_stream, L.hwp_read, L.hwp_write, L.hwp_empty, L.hwp_mfma_stream_operands):
+        f.restype = d
+    return L
+
+
+def test_mfma_stream_ceiling(hwp):
+    # 2560 tiles x 320 sub-steps of 16 MFMAs per wave = the workload-5 product's FLOPs
+    rows = []
+    for zero in (0, 1):
+        us = hwp.hwp_mfma_stream(2560, 320, zero, 10)
+        assert us > 0, "probe failed"
+        tf = GEMM_FLOP / us / 1e6
+        rows.append((zero, us, tf))
+        print("mfma stream (%s operands): %.1f us per product, %.0f TFLOP/s, %.3f of the fp16 peak"
+              % ("zero" if zero else "random", us, tf, tf / FP16_PEAK_TFLOPS), flush=True)
+    # the workload-5 product's own operand values (X with the transform, 1x16; W^T 16x16)
+    import numpy as np
+    import torch
+    from block_scaled_fp4_06_amd import nvfp4 as N
+    from block_scaled_fp4_06_amd import workloads as W
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    qa = N.quantize(dev(W.w3()), rht=True, rht_seed=W.RHT_SEED)
+    qw = N.quantize(dev(W.w5_weight()), blocking="16x16", with_transpose=True)
+    b = qw.transposed()
+    torch.cuda.synchronize()
+    us = hwp.hwp_mfma_stream_operands(qa.codes.data_ptr(), qa.scales.data_ptr(), b.codes.data_ptr(),
+                                      b.scales.data_ptr(), 8192, 20480, 5120, 320, 10)
+    assert us > 0, "probe failed"
+    tf = GEMM_FLOP / us / 1e6
+    rows.append((2, us, tf))
+    print("mfma stream (workload-5 operand values): %.1f us per product, %.0f TFLOP/s, %.3f of the "
+          "fp16 peak" % (us, tf, tf / FP16_PEAK_TFLOPS), flush=True)
+    for _, us, tf in rows:
+        assert 0.2 * FP16_PEAK_TFLOPS < tf < 1.05 * FP16_PEAK_TFLOPS
+
+
+def test_hbm_read_write_rates(hwp):
+    nbytes = 8192 * 5120 * 2   # the 84 MB activation tensor
+    for wgs in (1024, 10240):
+        us = hwp.hwp_read(nbytes, 7, wgs, 70)
+        assert us > 0, "probe failed"
+        gbps = nbytes / us / 1e3
+        print("read %d MB, %5d workgroups: %.2f us per launch, %.0f GB/s (%.3f of 8 TB/s)"
+              % (nbytes // 1000000, wgs, us, gbps, gbps / HBM_PEAK_GBPS), flush=True)
+        assert 1000 < gbps < 1.05 * HBM_PEAK_GBPS
+    names = ("ordinary", "non-temporal", "write-through (sc1)")
+    for mib in (16, 24, 64):
+        for pol in (0, 1, 2):
+            us = hwp.hwp_write(mib << 20, pol, 1024, 50)
+            assert us > 0, "probe failed"
+            gbps = (mib << 20) / us / 1e3
+            print("write %2d MiB, %-19s stores: %.2f us per launch, %.0f GB/s"
+                  % (mib, names[pol], us, gbps), flush=True)
+            assert gbps < 1.05 * HBM_PEAK_GBPS
+
+
+def test_launch_cost(hwp):
+    for wgs in (256, 1024):
+        us = hwp.hwp_empty(wgs, 100)
+        assert us > 0, "probe failed"
+        print("empty kernel, %4d workgroups: %.2f us per back-to-back launch" % (wgs, us), flush=True)
+        assert us < 50
