@@ -2,8 +2,9 @@
 //
 // Built by __graft_entry__.build() into tests/native/libhw_probe.so and driven by
 // tests/test_gpu_hw_ceilings.py.  None of this is part of libnvfp4.  Each entry point
-// allocates what it needs, times `reps` back-to-back launches between two events after a
-// few untimed ones, frees everything and returns microseconds per launch (negative on a HIP
+// allocates what it needs, times `reps` back-to-back launches between two events after
+// untimed ones (`warm` of them where the caller chooses: the clocks of this chip settle over
+// the first dozen or so GEMM-sized launches), frees everything and returns microseconds per launch (negative on a HIP
 // error).
 //
 //  * hwp_mfma_stream: the fp16 matrix-core instruction stream of the NVFP4 GEMM with its
@@ -219,13 +220,13 @@ double time_launches(F &&launch, int warm, int reps) {
 
 extern "C" {
 
-double hwp_mfma_stream(int workgroups, int substeps, int zero, int reps) {
-  if (workgroups < 1 || substeps < 2 || reps < 1) return -1.0;
+double hwp_mfma_stream(int workgroups, int substeps, int zero, int warm, int reps) {
+  if (workgroups < 1 || substeps < 2 || warm < 0 || reps < 1) return -1.0;
   float *out = nullptr;
   if (hipMalloc(&out, (size_t)workgroups * 256 * sizeof(float)) != hipSuccess) return -1.0;
   const double us = time_launches([&](int i) {
     mfma_stream_kernel<<<workgroups, 256>>>(out, substeps & ~1, 0x9E3779B9u + (uint32_t)i, zero);
-  }, 3, reps);
+  }, warm, reps);
   const bool ok = hipDeviceSynchronize() == hipSuccess;
   (void)hipFree(out);
   return ok ? us : -1.0;
@@ -234,16 +235,17 @@ double hwp_mfma_stream(int workgroups, int substeps, int zero, int reps) {
 // Device pointers of an NVFP4 product's operands (A M x K, 1x16 scales; B N x K, 16x16
 // scales); M and N multiples of 256, K of 32.  One workgroup per 256 x 256 tile.
 double hwp_mfma_stream_operands(const uint8_t *ac, const uint8_t *as, const uint8_t *bc,
-                                const uint8_t *bs, int M, int N, int K, int substeps, int reps) {
+                                const uint8_t *bs, int M, int N, int K, int substeps, int warm,
+                                int reps) {
   if (!ac || !as || !bc || !bs || M < 256 || N < 256 || K < 32 || M % 256 || N % 256 || K % 32 ||
-      substeps < 2 || reps < 1)
+      substeps < 2 || warm < 0 || reps < 1)
     return -1.0;
   const int wgs = (M / 256) * (N / 256);
   float *out = nullptr;
   if (hipMalloc(&out, (size_t)wgs * 256 * sizeof(float)) != hipSuccess) return -1.0;
   const double us = time_launches([&](int) {
     mfma_stream_operands_kernel<<<wgs, 256>>>(out, substeps & ~1, ac, as, bc, bs, M, N, K);
-  }, 3, reps);
+  }, warm, reps);
   const bool ok = hipDeviceSynchronize() == hipSuccess;
   (void)hipFree(out);
   return ok ? us : -1.0;
