@@ -17,6 +17,7 @@
 //    elements (an E2M1 magnitude times a 3-bit mantissa, random sign), so the multiplier
 //    inputs change every instruction as they do in the GEMM; `zero` feeds zeros instead.
 //    hwp_mfma_stream_operands runs it on the values of a real product's operands.
+//  * hwp_mfma_fp4_stream: the same for the MXFP4 GEMM's scaled FP4 instruction.
 //  * hwp_read: a streaming read of `bytes` (16 bytes per lane per load, each wave load
 //    covering 1 KiB), rotating over `nbuf` buffers so that the 256 MB Infinity Cache does
 //    not hold the input.
@@ -156,6 +157,76 @@ void mfma_stream_operands_kernel(float *out, int substeps, const uint8_t *ac, co
   out[blockIdx.x * 256u + threadIdx.x] = s;
 }
 
+// The MXFP4 GEMM's instruction stream: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands
+// FP4 (E2M1 codes, one E8M0 scale byte per 32 K-elements), the same 4 x 4 blocks of 32 x 32
+// per wave, 16 instructions per sub-step of K = 64.  mode 0: random codes and scale bytes
+// 124..131; mode 1: zeros (scale byte 127); mode 2: the codes and scales of MXFP4 operands
+// (A M x K, B N x K, K-contiguous, scales M x K/32 and N x K/32), K = 0..127 of each lane's
+// rows, the two 64-element halves alternating between sub-steps.
+typedef int v8i __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_fp4_stream_kernel(float *out, int substeps, int mode, uint32_t seed, const uint8_t *ac,
+                            const uint8_t *as, const uint8_t *bc, const uint8_t *bs, int N, int K) {
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const uint32_t lane_id = blockIdx.x * 256u + threadIdx.x;
+  v8i a[2][4], b[2][4];
+  int sa[2][4], sb[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v4i ca = {0, 0, 0, 0}, cb = {0, 0, 0, 0};
+      int xa = 127, xb = 127;
+      if (mode == 0) {
+        const uint32_t k = (lane_id * 8u + (uint32_t)(st * 4 + i)) * 8u;
+        ca = (v4i){(int)mix32(seed ^ k), (int)mix32(seed ^ (k + 1)), (int)mix32(seed ^ (k + 2)), (int)mix32(seed ^ (k + 3))};
+        cb = (v4i){(int)mix32(seed ^ (k + 4)), (int)mix32(seed ^ (k + 5)), (int)mix32(seed ^ (k + 6)), (int)mix32(seed ^ (k + 7))};
+        const uint32_t e = mix32(seed ^ ~k);
+        xa = 124 + (int)(e & 7u);
+        xb = 124 + (int)((e >> 3) & 7u);
+      } else if (mode == 2) {
+        const int tiles_n = N / 256;
+        const int64_t ra = (int64_t)((int)blockIdx.x / tiles_n) * 256 + wm * 128 + i * 32 + l32;
+        const int64_t rb = (int64_t)((int)blockIdx.x % tiles_n) * 256 + wn * 128 + i * 32 + l32;
+        const int64_t rowb = K / 2, groups = K / 32;
+        ca = *reinterpret_cast<const v4i *>(ac + ra * rowb + 32 * st + 16 * h);
+        cb = *reinterpret_cast<const v4i *>(bc + rb * rowb + 32 * st + 16 * h);
+        xa = as[ra * groups + 2 * st + h];
+        xb = bs[rb * groups + 2 * st + h];
+      }
+      a[st][i] = __builtin_shufflevector(ca, (v4i){0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+      b[st][i] = __builtin_shufflevector(cb, (v4i){0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+      sa[st][i] = xa;
+      sb[st][i] = xb;
+    }
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int t = 0; t < substeps; t += 2) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[st][i], b[st][j], acc[i][j], 4, 4, 0, sa[st][i], 0, sb[st][j]);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  out[lane_id] = sum;
+}
+
 __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ in, uint32_t n16,
                                                    uint32_t *out) {
   uint32_t acc = 0;
@@ -245,6 +316,27 @@ double hwp_mfma_stream_operands(const uint8_t *ac, const uint8_t *as, const uint
   if (hipMalloc(&out, (size_t)wgs * 256 * sizeof(float)) != hipSuccess) return -1.0;
   const double us = time_launches([&](int) {
     mfma_stream_operands_kernel<<<wgs, 256>>>(out, substeps & ~1, ac, as, bc, bs, M, N, K);
+  }, warm, reps);
+  const bool ok = hipDeviceSynchronize() == hipSuccess;
+  (void)hipFree(out);
+  return ok ? us : -1.0;
+}
+
+// MXFP4 stream: `workgroups` tiles of 256 x 256, `substeps` sub-steps of K = 64.  mode 2
+// reads operands (device pointers; M, N multiples of 256, K of 128): then workgroups must be
+// (M / 256) * (N / 256).
+double hwp_mfma_fp4_stream(int workgroups, int substeps, int mode, const uint8_t *ac,
+                           const uint8_t *as, const uint8_t *bc, const uint8_t *bs, int M, int N,
+                           int K, int warm, int reps) {
+  if (workgroups < 1 || substeps < 2 || mode < 0 || mode > 2 || warm < 0 || reps < 1) return -1.0;
+  if (mode == 2 && (!ac || !as || !bc || !bs || M < 256 || N < 256 || K < 128 || M % 256 ||
+                    N % 256 || K % 128 || workgroups != (M / 256) * (N / 256)))
+    return -1.0;
+  float *out = nullptr;
+  if (hipMalloc(&out, (size_t)workgroups * 256 * sizeof(float)) != hipSuccess) return -1.0;
+  const double us = time_launches([&](int i) {
+    mfma_fp4_stream_kernel<<<workgroups, 256>>>(out, substeps & ~1, mode, 0x85EBCA6Bu + (uint32_t)i,
+                                                ac, as, bc, bs, N, K);
   }, warm, reps);
   const bool ok = hipDeviceSynchronize() == hipSuccess;
   (void)hipFree(out);

@@ -8,6 +8,8 @@ library are read against:
   FLOPs of the 8192 x 20480 x 5120 product, with random values shaped like dequantized
   NVFP4 elements, with zeros, and with the values of the workload-5 operands themselves:
   what the chip sustains under its power limit, against the 2.5 PFLOP/s dense fp16 figure;
+* the same for the MXFP4 GEMM's scaled FP4 instruction, against the 10.1 PFLOP/s dense fp4
+  figure;
 * streaming HBM reads of the 84 MB activation tensor and streaming writes of 16-64 MiB with
   ordinary, non-temporal and write-through stores;
 * the cost of one back-to-back launch of an empty kernel.
@@ -26,6 +28,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROBE = os.path.join(ROOT, "tests", "native", "libhw_probe.so")
 GEMM_FLOP = 2.0 * 8192 * 20480 * 5120
 FP16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0
 HBM_PEAK_GBPS = 8000.0
 
 
@@ -44,7 +47,9 @@ def hwp():
     L.hwp_empty.argtypes = [i32, i32]
     P = ctypes.c_void_p
     L.hwp_mfma_stream_operands.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32]
-    for f in (L.hwp_mfma_stream, L.hwp_read, L.hwp_write, L.hwp_empty, L.hwp_mfma_stream_operands):
+    L.hwp_mfma_fp4_stream.argtypes = [i32, i32, i32, P, P, P, P, i32, i32, i32, i32, i32]
+    for f in (L.hwp_mfma_stream, L.hwp_read, L.hwp_write, L.hwp_empty, L.hwp_mfma_stream_operands,
+              L.hwp_mfma_fp4_stream):
         f.restype = d
     return L
 
@@ -97,6 +102,57 @@ def test_mfma_stream_ceiling(hwp):
         assert 0.2 * FP16_PEAK_TFLOPS < tf < 1.05 * FP16_PEAK_TFLOPS
     print("the GEMM runs at %.3f of the stream on its own operand values"
           % (best["mfma stream, workload-5 operand values"] / best["the NVFP4 GEMM itself (bf16 out)"]), flush=True)
+
+
+def test_mfma_fp4_stream_ceiling(hwp):
+    """The MXFP4 GEMM's instruction stream (v_mfma_scale_f32_32x32x64_f8f6f4, both operands
+    FP4, register-resident) over the workload-5 product's FLOPs (2560 tiles x 80 sub-steps of
+    K = 64), next to the library's MXFP4 GEMM on the workload-5 operands, against the 10.1
+    PFLOP/s dense fp4 figure."""
+    import numpy as np
+    import torch
+    from block_scaled_fp4_06_amd import nvfp4 as N
+    from block_scaled_fp4_06_amd import workloads as W
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    qa = N.mx_quantize(dev(W.w3()))
+    qb = N.mx_quantize(dev(np.ascontiguousarray(W.w5_weight().T)))
+    torch.cuda.synchronize()
+    ptrs = (qa.codes.data_ptr(), qa.scales.data_ptr(), qb.codes.data_ptr(), qb.scales.data_ptr())
+    c = torch.empty(8192, 20480, dtype=torch.bfloat16, device="cuda")
+
+    def gemm_us(warm):
+        for _ in range(warm):
+            N.mx_gemm(qa, qb, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            N.mx_gemm(qa, qb, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 100.0
+    runs = {
+        "fp4 mfma stream, random codes and scales":
+            lambda warm: hwp.hwp_mfma_fp4_stream(2560, 80, 0, None, None, None, None, 0, 0, 0, warm, 10),
+        "fp4 mfma stream, zeros":
+            lambda warm: hwp.hwp_mfma_fp4_stream(2560, 80, 1, None, None, None, None, 0, 0, 0, warm, 10),
+        "fp4 mfma stream, workload-5 MXFP4 operand values":
+            lambda warm: hwp.hwp_mfma_fp4_stream(2560, 80, 2, *ptrs, 8192, 20480, 5120, warm, 10),
+        "the MXFP4 GEMM itself (bf16 out)": gemm_us,
+    }
+    best = {}
+    for name, run in runs.items():
+        times = [run(20 if k == 0 else 2) for k in range(3)]
+        assert min(times) > 0, "probe failed"
+        best[name], med = min(times), float(np.median(times))
+        tf = GEMM_FLOP / best[name] / 1e6
+        print("%s: best %.1f us (median %.1f) per product, %.0f TFLOP/s, %.3f of the fp4 peak"
+              % (name, best[name], med, tf, tf / FP4_PEAK_TFLOPS), flush=True)
+        assert 0.05 * FP4_PEAK_TFLOPS < tf < 1.05 * FP4_PEAK_TFLOPS
+    print("the MXFP4 GEMM runs at %.3f of the stream on its own operand values"
+          % (best["fp4 mfma stream, workload-5 MXFP4 operand values"]
+             / best["the MXFP4 GEMM itself (bf16 out)"]), flush=True)
 
 
 def test_hbm_read_write_rates(hwp):
