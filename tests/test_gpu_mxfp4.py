@@ -119,7 +119,8 @@ def test_mx_dequantize_parity(out):
     codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
     scales = rng.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
     scales.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)
-    ref = oracle.mx_block_values_f64(codes, scales, rows, cols).astype(np.float32)
+    with np.errstate(over="ignore"):   # scale bytes near 254 overflow binary32: inf, as in the kernel
+        ref = oracle.mx_block_values_f64(codes, scales, rows, cols).astype(np.float32)
     q = N.MXFP4Tensor(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), rows, cols)
     if out == "f32":
         y = host(N.mx_dequantize(q, torch.float32))
