@@ -385,6 +385,35 @@ def test_dequantize_parity(blocking):
     assert torch.all(out[:, 528:] == -1.0)   # the row stride is honoured
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_dequantize_output_beyond_2gib(out_dtype):
+    """An output past 2 GiB takes the kernel's ordinary-store path (below 2 GiB the stores go
+    through a buffer resource over the output with 32-bit offsets): 32768 x 32768 elements
+    (4 GiB of fp32, 2 GiB of bf16) from random codes and E4M3 scales, sampled 16-row slices
+    (the last included) against the oracle."""
+    rows = cols = 32768
+    say("dequantize %dx%d to %s (ordinary-store path)" % (rows, cols, out_dtype))
+    g = torch.Generator(device="cuda").manual_seed(23)
+    codes = torch.randint(0, 256, (rows, cols // 2), dtype=torch.uint8, device="cuda", generator=g)
+    scales = torch.randint(0, 0x7F, (rows, cols // 16), dtype=torch.uint8, device="cuda", generator=g)
+    gd = torch.tensor([0.375], dtype=torch.float32, device="cuda")
+    q = N.NVFP4Tensor(codes, scales, gd, rows, cols, N.BLOCK_1x16)
+    f32 = out_dtype == "f32"
+    y = N.dequantize(q, torch.float32 if f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    for r in (0, 12336, rows // 2, rows - 16):   # 16-row slices (the oracle's row unit)
+        c = host(codes[r:r + 16])
+        sc = host(scales[r:r + 16])
+        if f32:
+            ref = oracle.dequantize(c, sc, np.float32(0.375), 16, cols)
+            assert np.array_equal(host(y[r:r + 16]).view(np.uint32), ref.view(np.uint32)), r
+        else:
+            ref = oracle.dequantize_bf16(c, sc, np.float32(0.375), 16, cols)
+            assert np.array_equal(host(y[r:r + 16].view(torch.int16)).view(np.uint16), ref), r
+    del y, codes, scales
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- GEMM
 def gemm_check(qa, qb, ref_a, ref_b, M, N_, K, rows=None):
     """Two-part gate: fp32 output within 1e-3 relative Frobenius of the binary64 product
