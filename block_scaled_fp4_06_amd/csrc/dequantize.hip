@@ -8,11 +8,11 @@
 //
 // One thread per part of a row group, 8 elements for bf16 output and 4 for fp32 (4 or 2
 // code bytes in, 16 bytes out), so each store instruction of a wave writes 1 KiB of
-// consecutive output; the stores write through the L2 (the agent-scope cache policy),
-// which on this chip writes a stream of whole lines faster than ordinary or non-temporal
-// stores (dequantize of workload 3 to bf16: 18.4-20.0 against 20.6-22.2 us with two
-// ordinary 16-byte stores per thread of a whole row group).  The kernel is HBM-bound
-// (9 bytes in, 32 or 64 out per 16 elements).
+// consecutive output, with non-temporal stores.  In the linear-layer step (quantize X,
+// quantize W, GEMM, dequantize X, repeated) ordinary or write-through stores of the 84 MB
+// output displace the weight from the 256 MB Infinity Cache, and the next weight quantize
+// pays for it (118-119 us against 101-104 us; step 1.410 against 1.394 ms).  The kernel
+// is HBM-bound (9 bytes in, 32 or 64 out per 16 elements).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -38,20 +38,15 @@ __device__ __forceinline__ void decode_byte(uint32_t w, float sbd, float s, floa
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
-// 16 bytes at byte offset `off` of y: with WT (an output of less than 2 GiB) through a
-// buffer resource over y with the agent-scope cache policy, otherwise an ordinary store.
-template <bool WT>
+// 16 bytes at byte offset `off` of y, non-temporal: the output is written once, and a
+// stream of ordinary or write-through stores would displace from the 256 MB Infinity Cache
+// what the caller reads next (see the file comment).
 __device__ __forceinline__ void store16(void *y, size_t off, v4i32 v) {
-  if (WT) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(y, (short)0, 0x7FFFFFFF, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
-  } else {
-    *reinterpret_cast<v4i32 *>(static_cast<uint8_t *>(y) + off) = v;
-  }
+  __builtin_nontemporal_store(v, reinterpret_cast<v4i32 *>(static_cast<uint8_t *>(y) + off));
 }
 
 // Part q of the output: row group q / P, elements E (q % P) .. + E - 1 of it.
-template <bool F32, bool B16, bool WT>
+template <bool F32, bool B16>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
     const float *__restrict__ global_dec, uint64_t nparts, uint32_t gpr, int64_t ld_y,
@@ -72,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
       decode_byte<1>(cw, sbd, s, v + 2);
       const v4i32 w = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
                        (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
-      store16<WT>(y, off * 4, w);
+      store16(y, off * 4, w);
     } else {
       const uint32_t cw = reinterpret_cast<const uint32_t *>(codes)[q];   // 4 code bytes
       float v[8];
@@ -84,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         h[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
-      store16<WT>(y, off * 2, (v4i32){(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+      store16(y, off * 2, (v4i32){(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
     }
   }
 }
@@ -98,17 +93,9 @@ hipError_t launch_dequantize(const DequantLaunch &d, hipStream_t stream) {
   uint64_t grid = (nparts + kThreads - 1) / kThreads;
   if (grid > 16384) grid = 16384;
   const uint32_t gpr = (uint32_t)(d.cols / 16);
-  // the last output element's byte offset + 1: write-through stores below 2 GiB
-  const uint64_t span = ((uint64_t)(d.rows - 1) * (uint64_t)d.ld_y + (uint64_t)d.cols) *
-                        (d.out_f32 ? 4u : 2u);
-  const bool wt = span <= 0x7FFFFFFFull;
 #define NVFP4_DQ(F, B)                                                                     \
-  do {                                                                                     \
-    if (wt) dequant_kernel<F, B, true><<<(uint32_t)grid, kThreads, 0, stream>>>(           \
-        d.codes, d.scales, d.global_dec, nparts, gpr, d.ld_y, d.y);                        \
-    else dequant_kernel<F, B, false><<<(uint32_t)grid, kThreads, 0, stream>>>(             \
-        d.codes, d.scales, d.global_dec, nparts, gpr, d.ld_y, d.y);                        \
-  } while (0)
+  dequant_kernel<F, B><<<(uint32_t)grid, kThreads, 0, stream>>>(                           \
+      d.codes, d.scales, d.global_dec, nparts, gpr, d.ld_y, d.y)
   if (d.out_f32) { if (d.blocking) NVFP4_DQ(true, true); else NVFP4_DQ(true, false); }
   else { if (d.blocking) NVFP4_DQ(false, true); else NVFP4_DQ(false, false); }
 #undef NVFP4_DQ

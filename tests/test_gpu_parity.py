@@ -387,12 +387,11 @@ def test_dequantize_parity(blocking):
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_dequantize_output_beyond_2gib(out_dtype):
-    """An output past 2 GiB takes the kernel's ordinary-store path (below 2 GiB the stores go
-    through a buffer resource over the output with 32-bit offsets): 32768 x 32768 elements
-    (4 GiB of fp32, 2 GiB of bf16) from random codes and E4M3 scales, sampled 16-row slices
-    (the last included) against the oracle."""
+    """Outputs past 2 GiB (64-bit element offsets): 32768 x 32768 elements (4 GiB of fp32,
+    2 GiB of bf16) from random codes and E4M3 scales, sampled 16-row slices (the last
+    included) against the oracle."""
     rows = cols = 32768
-    say("dequantize %dx%d to %s (ordinary-store path)" % (rows, cols, out_dtype))
+    say("dequantize %dx%d to %s" % (rows, cols, out_dtype))
     g = torch.Generator(device="cuda").manual_seed(23)
     codes = torch.randint(0, 256, (rows, cols // 2), dtype=torch.uint8, device="cuda", generator=g)
     scales = torch.randint(0, 0x7F, (rows, cols // 16), dtype=torch.uint8, device="cuda", generator=g)
