@@ -373,8 +373,10 @@ __device__ __forceinline__ float absmax16(const float v[16]) {
 
 // Output stores of the 1x16 kernels are streaming (non-temporal): every store instruction
 // writes whole lines (consecutive row groups), nothing reads them back in the kernel, and
-// lines left dirty in L2 would otherwise be written back when the kernel ends.  The 16x16
-// kernel writes 32-byte row pieces, which L2 must merge: it uses ordinary stores.
+// lines left dirty in the caches would otherwise be written back later, at the cost of
+// whatever runs then.  The 16x16 kernel stages x's codes in LDS so that they too leave in
+// whole row segments, non-temporal; the codes of x^T leave in 32- or 64-byte row pieces,
+// which the L2 must merge: ordinary stores.
 __device__ __forceinline__ void put2(uint8_t *p, uint2 v) {
   __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t *>(p));
   __builtin_nontemporal_store(v.y, reinterpret_cast<uint32_t *>(p) + 1);
@@ -676,12 +678,17 @@ __global__ __launch_bounds__(kThreads) void quant_1x16_sr_kernel(
 // ---------------------------------------------------------------- 16x16
 // A chunk is a block of up to G tile-rows x 16 tile columns (G x 16 rows, 256 columns); the
 // 16 lanes of a DPP row hold the 16 rows of a tile, one tile-row per step, and the tile
-// amax is a DPP max over the row.  Codes of x are stored per step; with TRANS the codes
-// of x^T come from an in-register 4-bit transpose and are assembled in LDS, so that each
-// of the chunk's 256 rows of x^T is written as one segment of 8 bytes per tile-row.
+// amax is a DPP max over the row.  Without TRANS the codes of x are stored per step.  With
+// TRANS they are staged in LDS (wbuf) and leave after the chunk as whole 128-byte row
+// segments with non-temporal stores (ordinary 32-byte pieces stayed dirty in the Infinity
+// Cache and slowed the next kernel's reads: workload-5 weight 109.5 -> 100.1 us, and the
+// activation quantize after it in the linear-layer step 46 -> 41 us); the codes of x^T
+// come from an in-register 4-bit transpose and are assembled in LDS, so that each of the
+// chunk's 256 rows of x^T is written as one segment of 8 bytes per tile-row.
 // G = 8 holds 64 MiB on chip (four workgroups per CU); a tensor that fits on chip in
 // chunks of G = 4 (five or six per CU) takes them: small tensors get twice the workgroups.
 constexpr int kT16 = 256;
+constexpr int kWS = 144;   // LDS bytes per staged 128-byte row of W's codes
 template <bool RHT, bool SR, bool TRANS, int G>
 __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t rk0,
@@ -692,6 +699,7 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
   constexpr int kTS = G * 8 + 8;   // LDS bytes per staged x^T row (+8 against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[TRANS ? 256 * kTS : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[TRANS ? 16 * G : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[TRANS ? G * 16 * kWS : 16];
   __shared__ float rtab[128];
   __shared__ uint32_t red[kT16 / 64];
   __shared__ uint32_t slot[2];
@@ -748,7 +756,10 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
         uint32_t w[8];
         if (SR) sr_draws(sr_base + (uint64_t)row * (uint64_t)cols + (uint64_t)tc * 16u, sk0, sk1, w);
         uint2 q = encode16<SR>(v, rr, w, (folds & kFold23) != 0);
-        if (col_ok) {
+        if (TRANS) {
+          *reinterpret_cast<uint2 *>(wbuf + (it * 16 + r) * kWS + tl * 8) = q;
+          if (col_ok && r == 0) scales[(size_t)trw * tpr + tc] = (uint8_t)sb;
+        } else if (col_ok) {
           *reinterpret_cast<uint2 *>(codes + row * (cols >> 1) + (int64_t)tc * 8) = q;
           if (r == 0) scales[(size_t)trw * tpr + tc] = (uint8_t)sb;
         }
@@ -761,6 +772,17 @@ __global__ __launch_bounds__(kT16) void quant_16x16_kernel(
     });
     if (TRANS) {
       __syncthreads();
+      // W's codes: nit * 16 rows of 16 pieces of 8 bytes (one per tile column); a wave's
+      // store writes 4 whole 128-byte row segments, non-temporal
+      for (uint32_t i = threadIdx.x; i < 256u * G; i += kT16) {
+        const uint32_t it = i >> 8, rr = (i >> 4) & 15u, pc = i & 15u;
+        const uint32_t ttc = bc * 16 + pc;
+        if (it < nit && ttc < tpr) {
+          const uint64_t w = *reinterpret_cast<const uint64_t *>(wbuf + (it * 16 + rr) * kWS + pc * 8);
+          const int64_t row = (int64_t)(tr0 + it) * 16 + rr;
+          __builtin_nontemporal_store(w, reinterpret_cast<uint64_t *>(codes + row * (cols >> 1) + (int64_t)ttc * 8));
+        }
+      }
       // 256 staged rows of x^T, nit * 8 bytes each: row j of the chunk is x^T row
       // bc*256 + j, bytes [tr0*8, tr0*8 + 8*nit)
       for (uint32_t i = threadIdx.x; i < 256u * G; i += kT16) {
