@@ -92,42 +92,51 @@ __device__ __forceinline__ void mx_decode_byte(uint32_t c, int e, float *v) {
   v[2 * B + 1] = __builtin_ldexpf(f[1], e);
 }
 
+// One thread per 16 bytes of output: 8 elements for bf16, 4 for fp32 (4 or 2 code bytes),
+// so each store instruction of a wave writes 1 KiB of consecutive output; non-temporal
+// stores (the output is written once).  Part q covers elements E q .. E q + E - 1 of the
+// row-major element order, whose 32-element block is (E q) / 32.
 template <bool F32, bool CONTIG>
-__global__ __launch_bounds__(256) void mx_dequant_kernel(const uint32_t *__restrict__ codes,
+__global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales,
-                                                         uint32_t c8, uint32_t nchunks, int64_t ld,
-                                                         void *__restrict__ y) {
-  for (uint32_t idx = blockIdx.x * 256u + threadIdx.x; idx < nchunks; idx += gridDim.x * 256u) {
-    const uint32_t c = codes[idx];
-    const uint32_t s = scales[idx >> 2];
+                                                         uint32_t cparts, uint64_t nparts,
+                                                         int64_t ld, void *__restrict__ y) {
+  typedef int v4i32 __attribute__((ext_vector_type(4)));
+  constexpr uint32_t E = F32 ? 4 : 8;
+  for (uint64_t q = (uint64_t)blockIdx.x * 256u + threadIdx.x; q < nparts;
+       q += (uint64_t)gridDim.x * 256u) {
+    const uint32_t c = F32 ? (uint32_t)reinterpret_cast<const uint16_t *>(codes)[q]
+                           : reinterpret_cast<const uint32_t *>(codes)[q];
+    const uint32_t s = scales[(q * E) >> 5];
     const int e = (int)s - 127;
     float v[8];
     mx_decode_byte<0>(c, e, v);
     mx_decode_byte<1>(c, e, v);
-    mx_decode_byte<2>(c, e, v);
-    mx_decode_byte<3>(c, e, v);
+    if (!F32) {
+      mx_decode_byte<2>(c, e, v);
+      mx_decode_byte<3>(c, e, v);
+    }
     if (s == 0xFFu) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = __builtin_nanf("");
     }
     uint64_t off;
     if (CONTIG) {
-      off = (uint64_t)idx * 8u;
+      off = q * E;
     } else {
-      const uint32_t r = idx / c8;
-      off = (uint64_t)r * (uint64_t)ld + (uint64_t)(idx - r * c8) * 8u;
+      const uint64_t r = q / cparts;
+      off = r * (uint64_t)ld + (q - r * cparts) * E;
     }
+    v4i32 w;
     if (F32) {
-      float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + off);
-      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      w = (v4i32){(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                  (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
+      __builtin_nontemporal_store(w, reinterpret_cast<v4i32 *>(reinterpret_cast<float *>(y) + off));
     } else {
-      uint32_t hw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        hw[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
-      *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + off) =
-          make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        w[i] = (int)((__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u));
+      __builtin_nontemporal_store(w, reinterpret_cast<v4i32 *>(reinterpret_cast<uint16_t *>(y) + off));
     }
   }
 }
@@ -525,13 +534,13 @@ hipError_t launch_mx_quantize(const MxQuantLaunch &q, hipStream_t stream) {
 }
 
 hipError_t launch_mx_dequantize(const MxDequantLaunch &d, hipStream_t stream) {
-  const uint64_t nchunks = (uint64_t)d.rows * (uint64_t)(d.cols / 8);
-  if (nchunks == 0) return hipSuccess;
-  const uint32_t grid = capped_grid(nchunks, 256, 8192);
-  const uint32_t c8 = (uint32_t)(d.cols / 8);
-  const uint32_t *codes = reinterpret_cast<const uint32_t *>(d.codes);
+  const uint32_t e = d.out_f32 ? 4u : 8u;
+  const uint64_t nparts = (uint64_t)d.rows * (uint64_t)(d.cols / e);
+  if (nparts == 0) return hipSuccess;
+  const uint32_t grid = capped_grid(nparts, 256, 16384);
+  const uint32_t cparts = (uint32_t)(d.cols / e);
   const bool contig = d.ld_y == d.cols;
-#define MX_DQ(F, C) mx_dequant_kernel<F, C><<<grid, 256, 0, stream>>>(codes, d.scales, c8, (uint32_t)nchunks, d.ld_y, d.y)
+#define MX_DQ(F, C) mx_dequant_kernel<F, C><<<grid, 256, 0, stream>>>(d.codes, d.scales, cparts, nparts, d.ld_y, d.y)
   if (d.out_f32) { if (contig) MX_DQ(true, true); else MX_DQ(true, false); }
   else { if (contig) MX_DQ(false, true); else MX_DQ(false, false); }
 #undef MX_DQ
